@@ -1,0 +1,438 @@
+"""Pins for the CPU oracle: it is checked against things other than itself --
+hand-derived fixtures, an exact-rational re-derivation of IEEE rounding,
+brute-force integer loops, independent library routines (torch casts,
+a symmetric eigensolver) and invariants of the method."""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# exact-rational IEEE rounding (independent of numpy's float arithmetic)
+# ---------------------------------------------------------------------------
+
+def round_to_format(x: Fraction, p: int, emin: int) -> Fraction:
+    """Round an exact rational to the nearest binary float with p significant
+    bits and minimum normal exponent emin (gradual underflow), ties to even,
+    unbounded exponent range above."""
+    if x == 0:
+        return Fraction(0)
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, emin)
+    ulp = Fraction(2) ** (e - p + 1)
+    n = a / ulp
+    m = math.floor(n)
+    rem = n - m
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and m % 2 == 1):
+        m += 1
+    return sign * m * ulp
+
+
+def f32r(x):
+    return round_to_format(Fraction(x), 24, -126)
+
+
+def f16r_sat(x):
+    r = round_to_format(Fraction(x), 11, -14)
+    if abs(r) > 65504:
+        r = Fraction(65504) * (1 if r > 0 else -1)
+    return r
+
+
+def rint_even(x: Fraction) -> int:
+    m = math.floor(x)
+    rem = x - m
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and m % 2 == 1):
+        m += 1
+    return m
+
+
+def brute_quantize_group(vals):
+    """One 64-group by the quantizer reading, in exact rationals."""
+    fr = [Fraction(float(v)) for v in vals]
+    amax = max(abs(v) for v in fr)
+    s = f16r_sat(f32r(amax / 7))
+    if s == 0:
+        return [0] * len(vals), s
+    inv = f32r(1 / s)
+    return [max(-7, min(7, rint_even(f32r(v * inv)))) for v in fr], s
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+
+def test_bf16_roundtrip_exhaustive():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    f = O.bf16_bits_to_f32(bits)
+    back = O.f32_to_bf16_bits(f)
+    finite = ~np.isnan(f)
+    assert np.array_equal(back[finite], bits[finite])
+    assert np.all(np.isnan(O.bf16_bits_to_f32(back[~finite])))
+
+
+def test_bf16_matches_torch_cast_random_and_ties():
+    rng = np.random.default_rng(7)
+    u = rng.integers(0, 1 << 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
+    # force a quarter of them to exact ties (low half = 0x8000)
+    u[: len(u) // 4] = (u[: len(u) // 4] & 0xFFFF0000) | 0x8000
+    f = u.view(np.float32)
+    f = f[np.isfinite(f)]
+    ours = O.f32_to_bf16_bits(f)
+    ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    # torch may turn values that overflow bf16 into inf the same way (RNE)
+    assert np.array_equal(ours, ref)
+
+
+def test_f16_saturating_known_values():
+    cases = {
+        65504.0: 65504.0, 65519.0: 65504.0, 65520.0: 65504.0, 1e6: 65504.0,
+        -1e6: -65504.0, 2.0 ** -24: 2.0 ** -24, 2.0 ** -25: 0.0,
+        3 * 2.0 ** -25: 2.0 ** -23, 1 + 2.0 ** -11: 1.0, 1 + 3 * 2.0 ** -11: 1 + 2.0 ** -9,
+    }
+    a = np.array(list(cases.keys()), dtype=np.float32)
+    h = O.f32_to_f16_sat(a).astype(np.float64)
+    assert list(h) == list(cases.values())
+
+
+def test_f16_matches_torch_half_cast():
+    rng = np.random.default_rng(8)
+    f = (rng.standard_normal(1 << 18) * np.exp2(rng.uniform(-30, 17, 1 << 18))).astype(np.float32)
+    ours = O.f32_to_f16_sat(f)
+    ref = torch.from_numpy(f).to(torch.float16).numpy()
+    fin = np.isfinite(ref)
+    assert np.array_equal(ours[fin].view(np.uint16), ref[fin].view(np.uint16))
+    assert np.all(np.abs(ours[~fin]) == np.float16(65504))
+
+
+# ---------------------------------------------------------------------------
+# quantizer and packing
+# ---------------------------------------------------------------------------
+
+def _golden(name):
+    with open(os.path.join(GOLD, name)) as fh:
+        return json.load(fh)
+
+
+def _group_from(case, n=64):
+    v = np.zeros(n, dtype=np.float32)
+    for k, hx in case["values"].items():
+        v[int(k)] = np.float32(float.fromhex(hx))
+    return v
+
+
+@pytest.mark.parametrize("case", _golden("int4_groups.json")["cases"], ids=lambda c: c["name"])
+def test_quantizer_golden(case):
+    v = _group_from(case)
+    q, s = O.quantize_groups(v[None, :])
+    assert int(s.view(np.uint16)[0, 0]) == int(case["scale_f16_bits"], 16)
+    want = np.zeros(64, dtype=np.int8)
+    for k, c in case["codes"].items():
+        want[int(k)] = c
+    assert np.array_equal(q[0], want)
+    packed = O.pack_int4(q)
+    want_b = np.zeros(32, dtype=np.uint8)
+    for k, b in case["packed_bytes"].items():
+        want_b[int(k)] = int(b, 16)
+    assert np.array_equal(packed[0], want_b)
+
+
+def test_quantizer_vs_exact_rational_bruteforce():
+    rng = np.random.default_rng(11)
+    groups = []
+    for i in range(48):
+        scale = 2.0 ** rng.integers(-30, 12)
+        g = (rng.standard_normal(64) * scale).astype(np.float32)
+        if i % 4 == 1:     # plant exact ties after scaling by a power-of-two s
+            s = 2.0 ** rng.integers(-10, 5)
+            k = rng.integers(-6, 6, 64) + 0.5
+            k[0] = 7
+            g = (k * s).astype(np.float32)
+        if i % 4 == 2:
+            g[rng.integers(0, 64, 40)] = 0
+        groups.append(g)
+    v = np.stack(groups)
+    q, s = O.quantize_groups(v)
+    for i in range(len(groups)):
+        codes, sref = brute_quantize_group(v[i])
+        assert Fraction(float(s[i, 0])) == sref
+        assert list(q[i]) == codes, i
+
+
+def test_quantizer_grid_lossless():
+    rng = np.random.default_rng(12)
+    for e in range(-14, 12):
+        s = 2.0 ** e
+        k = rng.integers(-7, 8, (4, 64))
+        k[:, 5] = 7 * np.where(rng.random(4) < 0.5, 1, -1)
+        q, sc = O.quantize_groups((k * s).astype(np.float32))
+        assert np.array_equal(q, k)
+        assert np.all(sc.astype(np.float64) == s)
+
+
+def test_quantizer_error_bound():
+    rng = np.random.default_rng(13)
+    v = (rng.standard_normal((64, 256)) * 3).astype(np.float32)
+    q, s = O.quantize_groups(v)
+    deq = q.reshape(64, 4, 64).astype(np.float64) * s.astype(np.float64)[:, :, None]
+    err = np.abs(deq - v.reshape(64, 4, 64))
+    assert np.all(err <= s.astype(np.float64)[:, :, None] * 0.5 * (1 + 1e-3))
+
+
+def test_pack_bytes_and_roundtrip():
+    q = np.array([[1, -1, -7, 7, 0, -8, 3, -3]], dtype=np.int8)
+    p = O.pack_int4(q)
+    assert list(p[0]) == [0xF1, 0x79, 0x80, 0xD3]
+    rng = np.random.default_rng(1)
+    q = rng.integers(-8, 8, (9, 128)).astype(np.int8)
+    assert np.array_equal(O.unpack_int4(O.pack_int4(q)), q)
+
+
+# ---------------------------------------------------------------------------
+# smoothing (stage 2) and SVD (stage 3)
+# ---------------------------------------------------------------------------
+
+def test_smoothing_closed_form():
+    ax = np.array([4.0, 1.0, 1e-7, 0.0], dtype=np.float32)
+    w = np.array([[1.0, -4.0, 0.5, 0.0], [-0.5, 2.0, -1.0, 0.0]], dtype=np.float32)
+    wb = O.f32_to_bf16_bits(w)
+    lam, sinv = O.smoothing(ax, wb)
+    # lambda = sqrt(max(ax,1e-5))/sqrt(max(aw,1e-5)): [2, 1/2, sqrt(1e-5), 1]
+    assert sinv[0] == np.float32(0.5) and sinv[1] == np.float32(2.0)
+    assert sinv[2] == np.float32(float.fromhex("0x1.3c3a4ep+8"))   # fp32 nearest sqrt(1e5)
+    assert sinv[3] == np.float32(1.0)
+
+
+def test_smoothing_preserves_product():
+    spec = synth.layer_spec("tiny")
+    lay = synth.gen_layer(spec)
+    x = O.bf16_bits_to_f32(lay["x"]).astype(np.float64)
+    ax = np.abs(O.bf16_bits_to_f32(lay["x"])).max(axis=0)
+    _, sinv = O.smoothing(ax, lay["w"])
+    w = O.bf16_bits_to_f32(lay["w"]).astype(np.float64).T
+    xh = x * sinv.astype(np.float64)[None, :]
+    wh = w / sinv.astype(np.float64)[:, None]
+    ref = x @ w
+    assert np.max(np.abs(xh @ wh - ref)) <= 1e-12 * np.max(np.abs(ref))
+    # the activation outliers shrink after migration
+    assert np.abs(xh).max() < 0.5 * np.abs(x).max()
+
+
+@pytest.fixture(scope="module")
+def tiny_pack():
+    spec = synth.layer_spec("tiny")
+    lay = synth.gen_layer(spec)
+    ax = np.abs(O.bf16_bits_to_f32(lay["x"])).max(axis=0)
+    pk = O.pack_weights(lay["w"], ax, spec.rank)
+    return spec, lay, ax, pk
+
+
+def test_svd_eckart_young_against_eigh(tiny_pack):
+    spec, lay, ax, pk = tiny_pack
+    wh = pk["w_hat"]
+    # singular values from a symmetric eigensolver of the Gram matrix
+    ev = np.sort(np.linalg.eigvalsh(wh @ wh.T))[::-1]
+    sig = np.sqrt(np.maximum(ev, 0))
+    r = spec.rank
+    l1 = O.bf16_bits_to_f32(pk["l1"]).astype(np.float64)
+    l2 = O.bf16_bits_to_f32(pk["l2"]).astype(np.float64)
+    low = l1 @ l2
+    s_low = np.linalg.eigvalsh(low @ low.T)[::-1][:r]
+    assert np.allclose(np.sqrt(np.maximum(s_low, 0)), sig[:r], rtol=2e-3)
+    tail = np.sum(sig[r:] ** 2)
+    res2 = np.sum((wh - low) ** 2)
+    assert abs(res2 - tail) <= 2e-2 * tail
+    # L2 rows orthonormal up to bf16 rounding
+    assert np.allclose(l2 @ l2.T, np.eye(r), atol=2e-2)
+
+
+def test_residual_reconstructs(tiny_pack):
+    _, _, _, pk = tiny_pack
+    l1 = O.bf16_bits_to_f32(pk["l1"]).astype(np.float64)
+    l2 = O.bf16_bits_to_f32(pk["l2"]).astype(np.float64)
+    recon = l1 @ l2 + pk["r"].astype(np.float64)
+    ulp = np.spacing(np.abs(pk["r"]).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(recon - pk["w_hat"]) <= ulp)
+
+
+def test_full_rank_gives_tiny_residual():
+    rng = np.random.default_rng(3)
+    w = O.f32_to_bf16_bits((rng.standard_normal((48, 64)) * 0.02).astype(np.float32))
+    ax = np.ones(64, dtype=np.float32)
+    pk = O.pack_weights(w, ax, 48)
+    assert np.linalg.norm(pk["r"]) <= 1e-2 * np.linalg.norm(pk["w_hat"])
+
+
+# ---------------------------------------------------------------------------
+# partials, dequant, whole layer
+# ---------------------------------------------------------------------------
+
+def test_group_partials_bruteforce():
+    rng = np.random.default_rng(5)
+    M, N, K = 5, 7, 192
+    qx = rng.integers(-7, 8, (M, K)).astype(np.int8)
+    qw = rng.integers(-7, 8, (N, K)).astype(np.int8)
+    P = O.group_partials(O.pack_int4(qx), O.pack_int4(qw))
+    for m in range(M):
+        for n in range(N):
+            for g in range(K // 64):
+                s = 0
+                for k in range(64 * g, 64 * g + 64):
+                    s += int(qx[m, k]) * int(qw[n, k])
+                assert P[m, n, g] == s
+    extreme = np.full((1, 64), 7, dtype=np.int8)
+    assert O.group_partials(O.pack_int4(extreme), O.pack_int4(-extreme))[0, 0, 0] == -3136
+
+
+def test_unit_scales_sum_partials():
+    rng = np.random.default_rng(6)
+    M, N, K = 8, 16, 256
+    qx = O.pack_int4(rng.integers(-7, 8, (M, K)))
+    qw = O.pack_int4(rng.integers(-7, 8, (N, K)))
+    ones_x = np.ones((K // 64, M), dtype=np.float16)
+    ones_w = np.ones((K // 64, N), dtype=np.float16)
+    P = O.group_partials(qx, qw)
+    acc = O.dequant_accumulate(P, ones_x, ones_w)
+    assert np.array_equal(acc, P.sum(axis=2).astype(np.float64))
+
+
+def _layer(spec):
+    lay = synth.gen_layer(spec)
+    ax = np.abs(O.bf16_bits_to_f32(lay["x"])).max(axis=0)
+    return lay, ax
+
+
+def test_rank0_is_plain_w4a4():
+    spec = synth.custom_spec(32, 256, 64, 0, seed=1)
+    lay, ax = _layer(spec)
+    pk = O.pack_weights(lay["w"], ax, 0)
+    out = O.svdq_linear(lay["x"], pk, lay["bias"])
+    # plain W4A4: dequantize both operands elementwise and multiply
+    a = O.quantize_act_lora_down(lay["x"], pk["smooth_inv"], pk["l1"])
+    qx = O.unpack_int4(a["xq"]).astype(np.float64)
+    qw = O.unpack_int4(pk["wq"]).astype(np.float64)
+    xd = qx * np.repeat(a["xs"].astype(np.float64).T, 64, axis=1)
+    wd = qw * np.repeat(pk["ws"].astype(np.float64).T, 64, axis=1)
+    ref = xd @ wd.T + O.bf16_bits_to_f32(lay["bias"]).astype(np.float64)[None, :]
+    assert np.allclose(out["y64"], ref, rtol=1e-12, atol=1e-12)
+    assert np.all(out["up"] == 0)
+
+
+def test_dequant_form_matches_per_group():
+    spec = synth.custom_spec(40, 320, 96, 16, seed=2)
+    lay, ax = _layer(spec)
+    pk = O.pack_weights(lay["w"], ax, 16)
+    a = O.svdq_linear(lay["x"], pk, lay["bias"], per_group=True)
+    b = O.svdq_linear(lay["x"], pk, lay["bias"], per_group=False)
+    assert np.allclose(a["y64"], b["y64"], rtol=1e-12, atol=1e-12 * np.abs(a["y64"]).max())
+
+
+def test_low_rank_branch_reduces_error_on_outliers():
+    """Stage 3 of the overview caption: the 16-bit low-rank branch eases the
+    4-bit quantization of the migrated weights."""
+    spec = synth.layer_spec("tiny")
+    lay, ax = _layer(spec)
+    ref = O.reference_linear(lay["x"], lay["w"], lay["bias"])
+    e0 = O.relative_error(O.svdq_linear(lay["x"], O.pack_weights(lay["w"], ax, 0))["y"], ref)
+    er = O.relative_error(O.svdq_linear(lay["x"], O.pack_weights(lay["w"], ax, spec.rank))["y"], ref)
+    assert er < e0
+    assert er < 0.2
+
+
+def test_smoothing_helps_w4a4_on_outliers():
+    """Stage 2 of the overview caption: migrating outliers from X to W makes
+    the activations easier to quantize.  Compare against no migration
+    (smooth_inv = 1) at rank 0."""
+    spec = synth.layer_spec("tiny")
+    lay, ax = _layer(spec)
+    ref = O.reference_linear(lay["x"], lay["w"], lay["bias"])
+    pk = O.pack_weights(lay["w"], ax, 0)
+    e_s = O.relative_error(O.svdq_linear(lay["x"], pk)["y"], ref)
+    flat = O.pack_weights(lay["w"], np.full_like(ax, 1.0), 0)
+    flat_ones = dict(flat)
+    flat_ones["smooth_inv"] = np.ones_like(flat["smooth_inv"])
+    w = O.bf16_bits_to_f32(lay["w"]).astype(np.float32)
+    q, s = O.quantize_groups(w)
+    flat_ones["wq"] = O.pack_int4(q)
+    flat_ones["ws"] = np.ascontiguousarray(s.T)
+    e_n = O.relative_error(O.svdq_linear(lay["x"], flat_ones)["y"], ref)
+    assert e_s < e_n
+
+
+def test_lora_merge_adds_xab():
+    spec = synth.custom_spec(48, 256, 128, 16, seed=4, lora_rank=16)
+    lay, ax = _layer(spec)
+    a_bits, b_bits = synth.gen_lora(spec)
+    pk = O.pack_weights(lay["w"], ax, 16)
+    base = O.svdq_linear(lay["x"], pk, lay["bias"])
+    l1n, l2n = O.merge_lora(pk["l1"], pk["l2"], pk["smooth_inv"], a_bits, b_bits)
+    pk2 = dict(pk, l1=l1n, l2=l2n)
+    merged = O.svdq_linear(lay["x"], pk2, lay["bias"])
+    x = O.bf16_bits_to_f32(lay["x"]).astype(np.float64)
+    xab = x @ O.bf16_bits_to_f32(a_bits).astype(np.float64) @ O.bf16_bits_to_f32(b_bits).astype(np.float64)
+    d = merged["y64"] - base["y64"]
+    assert np.max(np.abs(d - xab)) <= 2e-2 * np.max(np.abs(xab))
+    # the 4-bit residual is untouched
+    assert np.array_equal(pk2["wq"], pk["wq"]) and np.array_equal(pk2["ws"], pk["ws"])
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 rules
+# ---------------------------------------------------------------------------
+
+def test_mx_decode_table():
+    g = _golden("mxfp4_blocks.json")
+    codes = np.arange(16, dtype=np.uint8).reshape(1, 16)
+    codes = np.concatenate([codes, np.zeros((1, 16), np.uint8)], axis=1)
+    dec = O.mx_decode(codes, np.array([[127]], np.uint8))
+    assert list(dec[0, :16]) == g["decode_table"]
+    dec2 = O.mx_decode(codes, np.array([[130]], np.uint8))
+    assert list(dec2[0, :16]) == [8 * v for v in g["decode_table"]]
+
+
+def test_mx_ties_golden():
+    g = _golden("mxfp4_blocks.json")["ties"]
+    for v, c in zip(g["values"], g["codes"]):
+        blk = np.zeros((1, 32), np.float32)
+        blk[0, 0] = 6.0
+        blk[0, 1] = v
+        codes, sb = O.mx_quantize_blocks(blk)
+        assert sb[0, 0] == 127 and codes[0, 1] == c, v
+
+
+@pytest.mark.parametrize("case", _golden("mxfp4_blocks.json")["cases"], ids=lambda c: c["name"])
+def test_mx_blocks_golden(case):
+    v = _group_from(case, 32)
+    codes, sb = O.mx_quantize_blocks(v[None, :])
+    assert int(sb[0, 0]) == case["scale_byte"]
+    want = np.zeros(32, np.uint8)
+    for k, c in case["codes"].items():
+        want[int(k)] = c
+    assert np.array_equal(codes[0], want)
+
+
+def test_mx_power_of_two_grid_lossless():
+    rng = np.random.default_rng(21)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    for e in range(-20, 20, 3):
+        mags = grid[rng.integers(0, 8, (3, 32))]
+        mags[:, 0] = 6.0
+        vals = mags * np.where(rng.random((3, 32)) < 0.5, -1, 1) * 2.0 ** e
+        codes, sb = O.mx_quantize_blocks(vals.astype(np.float32))
+        assert np.all(sb == e + 127)
+        assert np.array_equal(O.mx_decode(codes, sb), vals)
