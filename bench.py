@@ -1,0 +1,230 @@
+"""Benchmark of the SVDQuant W4A4 + rank-32 linear layer on one MI355X.
+
+Workload: the FLUX.1 MLP pair at 1024x1024 (4096 image + 512 text tokens):
+fc1 4608 x 3072 -> 12288 and fc2 4608 x 12288 -> 3072, both rank 32, INT4
+groups of 64, bias.  One step runs both layers through the two fused kernels
+each (quantize + down projection, then 4-bit GEMM + up projection).  The fc2
+input is GELU(fc1 output) computed once before timing (not inside the step).
+
+Inputs are synthetic (seeded FLUX-shaped activations with planted outlier
+channels, random weights packed by the library's offline pack) and resident
+in HBM; four copies of every buffer are rotated so that the 256 MB
+Infinity Cache cannot hold a step's working set.
+
+Prints one JSON line.  `value` is the whole step's effective throughput
+(2*M*N*K summed over both layers / step time) in TOPS.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("fused W4A4+LoRA-r32 linear: µs/layer, TOPS & % INT8-MFMA roofline (FLUX MLP)")
+INT8_PEAK_TOPS = 5033.0        # 256 CU x 2.4 GHz x 8192 int8 ops/clk/CU (dense)
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "bit_quantized_diffusion_amd", "csrc", "svdq_kernels.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "k2_gemm_fc1_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--sets", type=int, default=4, help="rotated buffer sets")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=24, help="token rows in the oracle sample")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported "
+                          "(token rows shard across GPUs with no exchange; see the design notes)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_quantized_diffusion_amd as bq
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if not bq.device_check(0):
+        raise SystemExit(bq.status_string(bq.SVDQ_ERR_UNSUPPORTED_DEVICE))
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    def to_dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---------------- inputs and offline packs ----------------------------
+    s1, s2 = synth.layer_spec("fc1"), synth.layer_spec("fc2")
+    lay1 = synth.gen_layer(s1)
+    x1 = to_dev_bf16(lay1["x"])
+    ax1 = x1.float().abs().amax(dim=0).cpu().numpy().astype(np.float32)
+    t0 = time.time()
+    pk1 = bq.pack_weights(lay1["w"], ax1, s1.rank)
+    log(f"bench: packed fc1 ({s1.K}x{s1.N}, rank {s1.rank}) in {time.time() - t0:.1f} s")
+    L1 = bq.PackedLinear.from_host(pk1, lay1["bias"], s1.rank, device=dev)
+    y1 = bq.linear(x1, L1)
+    x2 = torch.nn.functional.gelu(y1.float(), approximate="tanh").to(torch.bfloat16)
+    ax2 = x2.float().abs().amax(dim=0).cpu().numpy().astype(np.float32)
+    idx2 = np.sort(np.argsort(-ax2, kind="stable")[: s2.n_outliers])
+    w2 = synth.gen_w(s2, idx2)
+    t0 = time.time()
+    pk2 = bq.pack_weights(w2, ax2, s2.rank)
+    log(f"bench: packed fc2 ({s2.K}x{s2.N}, rank {s2.rank}) in {time.time() - t0:.1f} s")
+    L2 = bq.PackedLinear.from_host(pk2, synth.gen_bias(s2), s2.rank, device=dev)
+    torch.cuda.synchronize()
+
+    M = s1.M
+
+    def clone_layer(L):
+        return bq.PackedLinear(L.K, L.N, L.rank, L.precision, L.smooth_inv.clone(),
+                               L.lora_down.clone(), L.lora_up.clone(), L.wq.clone(), L.ws.clone(),
+                               None if L.bias is None else L.bias.clone())
+
+    def buffers(L, x):
+        G = L.K // 64
+        return dict(L=clone_layer(L), x=x.clone(),
+                    xq=torch.empty((M, L.K // 2), dtype=torch.uint8, device=dev),
+                    xs=torch.empty((G, M), dtype=torch.float16, device=dev),
+                    la=torch.empty((M, L.rank), dtype=torch.float32, device=dev),
+                    y=torch.empty((M, L.N), dtype=torch.bfloat16, device=dev))
+
+    sets = [(buffers(L1, x1), buffers(L2, x2)) for _ in range(args.sets)]
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = {}
+
+    def run_layer(b, tag, record):
+        L = b["L"]
+        if record:
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record(stream)
+        bq.quantize_act_lora_down(b["x"], L.smooth_inv, L.lora_down, L.rank, xq=b["xq"], xs=b["xs"],
+                                  lora_act=b["la"])
+        if record:
+            e1.record(stream)
+        bq.gemm_w4a4_lora_up(b["xq"], b["xs"], L.wq, L.ws, b["la"], L.lora_up, L.bias, M, L.N, L.K,
+                             L.rank, y=b["y"])
+        if record:
+            e2.record(stream)
+            ev.setdefault(tag, []).append((e0, e1, e2))
+
+    def step(i, record):
+        b1, b2 = sets[i % len(sets)]
+        run_layer(b1, "fc1", record)
+        run_layer(b2, "fc2", record)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    log(f"bench: warmup {args.warmup} steps done")
+
+    # timed region: host clock around exactly `steps` steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    log(f"bench: timed {args.steps} steps in {elapsed * 1e3:.2f} ms")
+
+    def avg_us(tag, a, b):
+        return 1e3 * float(np.mean([x[a].elapsed_time(x[b]) for x in ev[tag]]))
+
+    per = {}
+    ops_total = 0.0
+    for tag, s in (("fc1", s1), ("fc2", s2)):
+        k1 = avg_us(tag, 0, 1)
+        k2 = avg_us(tag, 1, 2)
+        ops = 2.0 * s.M * s.N * s.K
+        ops_total += ops
+        per[tag] = {"M": s.M, "K": s.K, "N": s.N, "rank": s.rank,
+                    "us_k1": round(k1, 2), "us_k2": round(k2, 2), "us_layer": round(k1 + k2, 2),
+                    "tops": round(ops / ((k1 + k2) * 1e-6) / 1e12, 1),
+                    "pct_int8_roofline": round(100 * ops / ((k1 + k2) * 1e-6) / 1e12 / INT8_PEAK_TOPS, 2)}
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = ops_total / (ms_per_step * 1e-3) / 1e12
+
+    # roofline of the dominant kernel: the fc1 4-bit GEMM
+    k2_us = per["fc1"]["us_k2"]
+    achieved = 2.0 * s1.M * s1.N * s1.K / (k2_us * 1e-6) / 1e12
+    traffic = None
+    if os.path.exists(COUNTERS):
+        with open(COUNTERS) as fh:
+            c = json.load(fh)
+        if c.get("kernel_sha") == kernel_sha():
+            traffic = c.get("hbm_bytes_per_launch")
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic,
+                "kernel": "k2_gemm_int4 (fc1 4608x3072x12288)", "ops": "int8 MFMA ops"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(lay1, pk1, s1, args.cpu_rows)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "FLUX.1 MLP pair at 1024x1024: fc1 4608x3072->12288 + fc2 4608x12288->3072, "
+                               "rank 32, int4 g64 W4A4, bf16 in/out, bias",
+                   "M": s1.M, "layers": per, "rotated_sets": args.sets, "parallelism": "single GPU"},
+        "us_per_layer": {k: v["us_layer"] for k, v in per.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(lay1, pk1, spec, rows):
+    """The oracle's online path (both fused kernels' steps) for `rows` token
+    rows of fc1 on the host cores, scaled to TOPS."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threads = os.cpu_count()
+    sel = np.linspace(0, spec.M - 1, rows).astype(np.int64)
+    x = np.ascontiguousarray(lay1["x"][sel])
+    l1 = np.ascontiguousarray(pk1["lora_down"].T)
+    l2 = np.ascontiguousarray(pk1["lora_up"].T)
+    t0 = time.perf_counter()
+    a = O.quantize_act_lora_down(x, pk1["smooth_inv"], l1)
+    O.gemm_w4a4_lora_up(a["xq"], a["xs"], pk1["wq"], pk1["ws"], a["t"], l2, lay1["bias"])
+    dt = time.perf_counter() - t0
+    ops = 2.0 * rows * spec.N * spec.K
+    log(f"bench: cpu oracle {rows} rows of fc1 in {dt:.1f} s")
+    return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows} of {spec.M} token rows of fc1 ({spec.K}->{spec.N}, rank {spec.rank}), "
+                      f"quantize+down and per-group GEMM+up, {dt:.1f} s",
+            "us_per_layer_equiv": round(dt / rows * spec.M * 1e6, 1)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,232 @@
+"""SVDQuant W4A4 linear layer for AMD Instinct MI355X (gfx950).
+
+A thin binding over the C ABI of ``libsvdq.so`` (``include/svdq.h``).  It only
+marshals arguments: torch tensors supply device memory and the current HIP
+stream, every step of the layer runs in the library's HIP kernels, and the
+offline pack runs in the library's C++ code.  A missing library is an import
+error; there is no fallback.
+
+    Y = X^ L1 L2 + dequant(Q4(X^) Q4(R)^T) + b,   X^ = X diag(lambda)^-1
+
+(model card "svdq-int4-flux.1-dev": "Overview of SVDQuant" caption, stages
+2-3; Nunchaku engine caption (b): the two fused kernels.)
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from ._lib import (INT4, MXFP4, SVDQ_ERR_HIP, SVDQ_ERR_INVALID_ARG,  # noqa: F401
+                   SVDQ_ERR_SHAPE, SVDQ_ERR_UNSUPPORTED_DEVICE, SVDQ_OK,
+                   EXPORTED, LIB_PATH, SvdqError, check, lib, status_string)
+
+__all__ = [
+    "INT4", "MXFP4", "SvdqError", "lib", "LIB_PATH", "status_string",
+    "version", "device_check", "packed_sizes", "act_sizes", "pack_weights",
+    "quantize_act_lora_down", "gemm_w4a4_lora_up", "debug_group_partials",
+    "PackedLinear", "linear",
+]
+
+
+def version() -> int:
+    return lib.svdq_version()
+
+
+def device_check(device: int = 0) -> bool:
+    return lib.svdq_device_check(int(device)) == SVDQ_OK
+
+
+def packed_sizes(K: int, N: int, rank: int, precision: int = INT4):
+    out = (ctypes.c_size_t * 5)()
+    check(lib.svdq_packed_sizes(K, N, rank, precision, out))
+    return tuple(int(v) for v in out)
+
+
+def act_sizes(M: int, K: int, rank: int, precision: int = INT4):
+    out = (ctypes.c_size_t * 3)()
+    check(lib.svdq_act_sizes(M, K, rank, precision, out))
+    return tuple(int(v) for v in out)
+
+
+def _np_ptr(a: Optional[np.ndarray]):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def pack_weights(w_bf16: np.ndarray, act_absmax: np.ndarray, rank: int,
+                 precision: int = INT4, want_residual: bool = False) -> dict:
+    """Offline pack on the CPU.  w_bf16: uint16 bf16 bits [N][K] (nn.Linear
+    layout); act_absmax: float32 [K].  Returns host numpy arrays:
+    smooth_inv [K] f32, lora_down [rank][K] u16, lora_up [N][rank] u16,
+    wq [N][K/2] u8, ws [K/64][N] f16 (INT4) or [K/32][N] u8 (MXFP4), and the
+    residual r [K][N] f32 when asked for."""
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    ax = np.ascontiguousarray(act_absmax, dtype=np.float32)
+    if w.ndim != 2 or ax.ndim != 1 or ax.shape[0] != w.shape[1]:
+        raise ValueError("w_bf16 must be [N][K] and act_absmax [K]")
+    N, K = w.shape
+    packed_sizes(K, N, rank, precision)          # validates the shape
+    out = dict(
+        smooth_inv=np.empty(K, np.float32),
+        lora_down=np.empty((rank, K), np.uint16),
+        lora_up=np.empty((N, rank), np.uint16),
+        wq=np.empty((N, K // 2), np.uint8),
+        ws=(np.empty((K // 64, N), np.float16) if precision == INT4
+            else np.empty((K // 32, N), np.uint8)),
+    )
+    r = np.empty((K, N), np.float32) if want_residual else None
+    check(lib.svdq_pack_weights(
+        _np_ptr(w), _np_ptr(ax), K, N, rank, precision,
+        _np_ptr(out["smooth_inv"]), _np_ptr(out["lora_down"]) if rank else None,
+        _np_ptr(out["lora_up"]) if rank else None, _np_ptr(out["wq"]),
+        _np_ptr(out["ws"]), _np_ptr(r)))
+    if want_residual:
+        out["r"] = r
+    return out
+
+
+# ---------------------------------------------------------------------------
+# device calls (torch tensors as device memory)
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dptr(t, dtype, shape, name):
+    """Device pointer of a contiguous CUDA tensor with the given dtype/shape."""
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name}: expected a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: tensor must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _scale_dtype(precision):
+    torch = _torch()
+    return torch.float16 if precision == INT4 else torch.uint8
+
+
+def _groups(K, precision):
+    return K // 64 if precision == INT4 else K // 32
+
+
+def quantize_act_lora_down(x, smooth_inv, lora_down, rank: int, precision: int = INT4,
+                           xq=None, xs=None, lora_act=None):
+    """First fused kernel.  x: bf16 [M][K]; smooth_inv: f32 [K];
+    lora_down: bf16 [rank][K] or None when rank == 0.
+    Returns (xq u8 [M][K/2], xs [K/g][M], lora_act f32 [M][rank] or None)."""
+    torch = _torch()
+    M, K = x.shape
+    dev = x.device
+    if xq is None:
+        xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    if xs is None:
+        xs = torch.empty((_groups(K, precision), M), dtype=_scale_dtype(precision), device=dev)
+    if rank and lora_act is None:
+        lora_act = torch.empty((M, rank), dtype=torch.float32, device=dev)
+    check(lib.svdq_quantize_act_lora_down(
+        _dptr(x, torch.bfloat16, (M, K), "x"), M, K,
+        _dptr(smooth_inv, torch.float32, (K,), "smooth_inv"),
+        _dptr(lora_down, torch.bfloat16, (rank, K), "lora_down") if rank else None,
+        rank, precision,
+        _dptr(xq, torch.uint8, (M, K // 2), "xq"),
+        _dptr(xs, _scale_dtype(precision), (_groups(K, precision), M), "xs"),
+        _dptr(lora_act, torch.float32, (M, rank), "lora_act") if rank else None,
+        _stream(dev)))
+    return xq, xs, (lora_act if rank else None)
+
+
+def gemm_w4a4_lora_up(xq, xs, wq, ws, lora_act, lora_up, bias, M: int, N: int, K: int,
+                      rank: int, precision: int = INT4, y=None):
+    """Second fused kernel.  Returns y bf16 [M][N]."""
+    torch = _torch()
+    dev = xq.device
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    sd = _scale_dtype(precision)
+    G = _groups(K, precision)
+    check(lib.svdq_gemm_w4a4_lora_up(
+        _dptr(xq, torch.uint8, (M, K // 2), "xq"), _dptr(xs, sd, (G, M), "xs"),
+        _dptr(wq, torch.uint8, (N, K // 2), "wq"), _dptr(ws, sd, (G, N), "ws"),
+        _dptr(lora_act, torch.float32, (M, rank), "lora_act") if rank else None,
+        _dptr(lora_up, torch.bfloat16, (N, rank), "lora_up") if rank else None,
+        _dptr(bias, torch.bfloat16, (N,), "bias"),
+        _dptr(y, torch.bfloat16, (M, N), "y"),
+        M, N, K, rank, precision, _stream(dev)))
+    return y
+
+
+def debug_group_partials(xq, wq, M: int, N: int, K: int, m0: int, n0: int, mt: int, nt: int, out=None):
+    """Exact INT4 per-group partials for a window: int32 [mt][nt][K/64]."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((mt, nt, K // 64), dtype=torch.int32, device=xq.device)
+    check(lib.svdq_debug_group_partials(
+        _dptr(xq, torch.uint8, (M, K // 2), "xq"), _dptr(wq, torch.uint8, (N, K // 2), "wq"),
+        M, N, K, m0, n0, mt, nt, _dptr(out, torch.int32, (mt, nt, K // 64), "out"),
+        _stream(xq.device)))
+    return out
+
+
+@dataclass
+class PackedLinear:
+    """Packed weights of one layer, resident on a device."""
+    K: int
+    N: int
+    rank: int
+    precision: int
+    smooth_inv: object
+    lora_down: object
+    lora_up: object
+    wq: object
+    ws: object
+    bias: object = None
+
+    @classmethod
+    def from_host(cls, packed: dict, bias_bf16: Optional[np.ndarray], rank: int,
+                  precision: int = INT4, device="cuda"):
+        torch = _torch()
+        N, K2 = packed["wq"].shape
+
+        def dev(a, dtype):
+            t = torch.from_numpy(np.ascontiguousarray(a))
+            if dtype in (torch.bfloat16,):
+                t = t.view(torch.int16).view(torch.bfloat16)
+            elif dtype == torch.float16 and t.dtype != torch.float16:
+                t = t.view(torch.float16)
+            return t.to(device)
+
+        return cls(
+            K=K2 * 2, N=N, rank=rank, precision=precision,
+            smooth_inv=dev(packed["smooth_inv"], torch.float32),
+            lora_down=dev(packed["lora_down"], torch.bfloat16) if rank else None,
+            lora_up=dev(packed["lora_up"], torch.bfloat16) if rank else None,
+            wq=dev(packed["wq"], torch.uint8),
+            ws=dev(packed["ws"], torch.float16 if precision == INT4 else torch.uint8),
+            bias=None if bias_bf16 is None else dev(bias_bf16, torch.bfloat16),
+        )
+
+
+def linear(x, layer: PackedLinear, y=None):
+    """Y = layer(x) for x bf16 [M][K] on the device: both fused kernels."""
+    M = x.shape[0]
+    xq, xs, la = quantize_act_lora_down(x, layer.smooth_inv, layer.lora_down, layer.rank, layer.precision)
+    return gemm_w4a4_lora_up(xq, xs, layer.wq, layer.ws, la, layer.lora_up, layer.bias,
+                             M, layer.N, layer.K, layer.rank, layer.precision, y=y)

@@ -1,0 +1,160 @@
+// C ABI entry points of libsvdq.so: argument and device validation, then the
+// kernel launchers.  Nothing here throws; every failure is a status code.
+//
+// The device check follows the "Hardware support" section of the blog
+// "Nunchaku 4-bit inference in Diffusers": the capability of the GPU is
+// checked when the layer is used and an unsupported GPU gets a clear error
+// instead of wrong output.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+#include <mutex>
+
+#include "svdq_internal.h"
+
+using namespace svdq;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = not probed yet, 1 = gfx950, 2 = not usable
+std::atomic<int> g_dev_state[kMaxDevices];
+std::mutex g_dev_mutex;
+
+int probe_device(int device) {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return SVDQ_ERR_UNSUPPORTED_DEVICE;
+  if (device < 0 || device >= count || device >= kMaxDevices) return SVDQ_ERR_UNSUPPORTED_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return SVDQ_ERR_UNSUPPORTED_DEVICE;
+  return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? SVDQ_OK : SVDQ_ERR_UNSUPPORTED_DEVICE;
+}
+
+int current_device_ok() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return SVDQ_ERR_UNSUPPORTED_DEVICE;
+  }
+  return svdq_device_check(dev);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(int e) { return e == 0 ? SVDQ_OK : SVDQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int svdq_version(void) { return 100; }
+
+const char* svdq_status_string(int status) {
+  switch (status) {
+    case SVDQ_OK: return "svdq: ok";
+    case SVDQ_ERR_INVALID_ARG: return "svdq: invalid argument (NULL or misaligned pointer, or unknown precision)";
+    case SVDQ_ERR_SHAPE: return "svdq: unsupported shape (check M, N >= 1, K and rank rules)";
+    case SVDQ_ERR_UNSUPPORTED_DEVICE: return "svdq: no usable gfx950 (MI355X) device; the 4-bit kernels need gfx950";
+    case SVDQ_ERR_HIP: return "svdq: HIP runtime error (launch failed)";
+    default: return "svdq: unknown status";
+  }
+}
+
+int svdq_device_check(int device) {
+  if (device < 0 || device >= kMaxDevices) return SVDQ_ERR_UNSUPPORTED_DEVICE;
+  int s = g_dev_state[device].load(std::memory_order_acquire);
+  if (s == 0) {
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    s = g_dev_state[device].load(std::memory_order_relaxed);
+    if (s == 0) {
+      s = probe_device(device) == SVDQ_OK ? 1 : 2;
+      (void)hipGetLastError();
+      g_dev_state[device].store(s, std::memory_order_release);
+    }
+  }
+  return s == 1 ? SVDQ_OK : SVDQ_ERR_UNSUPPORTED_DEVICE;
+}
+
+int svdq_packed_sizes(int K, int N, int rank, int precision, size_t* out) {
+  int st = check_precision(precision);
+  if (st) return st;
+  if (!out) return SVDQ_ERR_INVALID_ARG;
+  if (N < 1) return SVDQ_ERR_SHAPE;
+  if ((st = check_k(K, precision))) return st;
+  if ((st = check_rank(rank, K, N))) return st;
+  const size_t k = static_cast<size_t>(K), n = static_cast<size_t>(N), r = static_cast<size_t>(rank);
+  out[0] = k * 4;
+  out[1] = r * k * 2;
+  out[2] = n * r * 2;
+  out[3] = n * k / 2;
+  out[4] = precision == SVDQ_INT4 ? (k / kInt4Group) * n * 2 : (k / kMxBlock) * n;
+  return SVDQ_OK;
+}
+
+int svdq_act_sizes(int M, int K, int rank, int precision, size_t* out) {
+  int st = check_precision(precision);
+  if (st) return st;
+  if (!out) return SVDQ_ERR_INVALID_ARG;
+  if (M < 1) return SVDQ_ERR_SHAPE;
+  if ((st = check_k(K, precision))) return st;
+  if ((st = check_rank(rank, K, K))) return st;
+  const size_t m = static_cast<size_t>(M), k = static_cast<size_t>(K), r = static_cast<size_t>(rank);
+  out[0] = m * k / 2;
+  out[1] = precision == SVDQ_INT4 ? (k / kInt4Group) * m * 2 : (k / kMxBlock) * m;
+  out[2] = m * r * 4;
+  return SVDQ_OK;
+}
+
+int svdq_quantize_act_lora_down(const void* x, int M, int K, const float* smooth_inv, const void* lora_down,
+                                int rank, int precision, uint8_t* xq, void* xs, float* lora_act, void* stream) {
+  int st = check_precision(precision);
+  if (st) return st;
+  if (!x || !smooth_inv || !xq || !xs) return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!lora_down || !lora_act)) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(smooth_inv) || !aligned16(xq) || !aligned16(xs)) return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!aligned16(lora_down) || !aligned16(lora_act))) return SVDQ_ERR_INVALID_ARG;
+  if (M < 1) return SVDQ_ERR_SHAPE;
+  if ((st = check_k(K, precision))) return st;
+  if ((st = check_rank(rank, K, K))) return st;
+  if (precision != SVDQ_INT4) return SVDQ_ERR_INVALID_ARG;
+  if ((st = current_device_ok())) return st;
+  return hip_status(svdq_launch_quantize_act_lora_down(x, M, K, smooth_inv, lora_down, rank, precision, xq, xs,
+                                                       lora_act, stream));
+}
+
+int svdq_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs, const uint8_t* wq, const void* ws,
+                           const float* lora_act, const void* lora_up, const void* bias, void* y, int M, int N,
+                           int K, int rank, int precision, void* stream) {
+  int st = check_precision(precision);
+  if (st) return st;
+  if (!xq || !xs || !wq || !ws || !y) return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!lora_act || !lora_up)) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(wq) || !aligned16(ws) || !aligned16(y))
+    return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!aligned16(lora_act) || !aligned16(lora_up))) return SVDQ_ERR_INVALID_ARG;
+  if (bias && !aligned16(bias)) return SVDQ_ERR_INVALID_ARG;
+  if (M < 1 || N < 1) return SVDQ_ERR_SHAPE;
+  if ((st = check_k(K, precision))) return st;
+  if ((st = check_rank(rank, K, N))) return st;
+  if (precision != SVDQ_INT4) return SVDQ_ERR_INVALID_ARG;
+  if ((st = current_device_ok())) return st;
+  return hip_status(svdq_launch_gemm_w4a4_lora_up(xq, xs, wq, ws, lora_act, lora_up, bias, y, M, N, K, rank,
+                                                  precision, stream));
+}
+
+int svdq_debug_group_partials(const uint8_t* xq, const uint8_t* wq, int M, int N, int K, int m0, int n0, int mt,
+                              int nt, int32_t* out, void* stream) {
+  if (!xq || !wq || !out) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(xq) || !aligned16(wq) || !aligned16(out)) return SVDQ_ERR_INVALID_ARG;
+  if (M < 1 || N < 1 || mt < 1 || nt < 1) return SVDQ_ERR_SHAPE;
+  int st = check_k(K, SVDQ_INT4);
+  if (st) return st;
+  if (m0 < 0 || n0 < 0 || m0 + static_cast<long long>(mt) > M || n0 + static_cast<long long>(nt) > N)
+    return SVDQ_ERR_SHAPE;
+  if ((st = current_device_ok())) return st;
+  return hip_status(svdq_launch_debug_group_partials(xq, wq, M, N, K, m0, n0, mt, nt, out, stream));
+}
+
+}  // extern "C"

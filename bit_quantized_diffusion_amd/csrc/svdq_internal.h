@@ -1,0 +1,50 @@
+// Internal declarations shared by the host-side translation units of
+// libsvdq.so.  Not part of the public ABI (that is include/svdq.h).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/svdq.h"
+
+namespace svdq {
+
+constexpr int kInt4Group = 64;    // INT4 quantization group along K
+constexpr int kMxBlock = 32;      // MXFP4 block along K
+constexpr int kMaxRank = 256;
+
+// Number of host threads for the offline pack.
+int host_threads();
+
+// Shape rules of the ABI; return SVDQ_OK or SVDQ_ERR_SHAPE / _INVALID_ARG.
+int check_precision(int precision);
+int check_k(int K, int precision);
+int check_rank(int rank, int K, int N);
+
+// Host-side number-format helpers used by the offline pack.
+uint16_t f32_to_bf16_bits(float f);
+float bf16_bits_to_f32(uint16_t b);
+uint16_t f32_to_f16_sat_bits(float f);
+float f16_bits_to_f32(uint16_t h);
+
+}  // namespace svdq
+
+// Kernel launchers (defined in svdq_kernels.hip).  They assume validated
+// arguments and return a hipError_t value as int.
+extern "C" {
+int svdq_launch_quantize_act_lora_down(const void* x, int M, int K,
+                                       const float* smooth_inv,
+                                       const void* lora_down, int rank,
+                                       int precision, uint8_t* xq, void* xs,
+                                       float* lora_act, void* stream);
+int svdq_launch_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs,
+                                  const uint8_t* wq, const void* ws,
+                                  const float* lora_act, const void* lora_up,
+                                  const void* bias, void* y, int M, int N,
+                                  int K, int rank, int precision,
+                                  void* stream);
+int svdq_launch_debug_group_partials(const uint8_t* xq, const uint8_t* wq,
+                                     int M, int N, int K, int m0, int n0,
+                                     int mt, int nt, int32_t* out,
+                                     void* stream);
+}

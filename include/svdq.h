@@ -1,0 +1,178 @@
+/*
+ * svdq.h -- C ABI of the SVDQuant W4A4 linear layer for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The layer computes
+ *
+ *     Y = X^ L1 L2 + dequant( Q4(X^) Q4(R)^T ) + b,
+ *     X^ = X diag(lambda)^-1,   W^ = diag(lambda) W = L1 L2 + R
+ *
+ * (model card "svdq-int4-flux.1-dev", "Overview of SVDQuant" caption:
+ * stage 2 migrates activation outliers into the weights, stage 3 splits the
+ * weights by SVD into a 16-bit low-rank branch and a 4-bit residual; the
+ * SVDQuant abstract: W4A4 with a high-precision low-rank branch).
+ *
+ * It runs as two fused kernels (same card, Nunchaku engine caption (b)):
+ *   svdq_quantize_act_lora_down  smoothing + 4-bit activation quantization +
+ *                                down projection X^ L1, reading X once;
+ *   svdq_gemm_w4a4_lora_up       4-bit GEMM + per-group dequant + up
+ *                                projection + bias, writing Y once.
+ * The weights are packed offline on the CPU by svdq_pack_weights.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All buffers are allocated and owned by the caller.  The library keeps
+ *    no per-call state and allocates nothing on the two hot calls.  Host
+ *    pointers are marked (host), device pointers (dev).
+ *  - Matrices are dense, row-major, contiguous.  bf16 and fp16 values are
+ *    passed as their 16-bit patterns.
+ *  - W is given in nn.Linear layout [N][K] (out x in); the blog "Nunchaku
+ *    4-bit inference in Diffusers" ("Introducing Nunchaku Lite") replaces
+ *    nn.Linear modules with the quantized layer.  The low-rank factors are
+ *    stored the same way: lora_down = L1^T as [rank][K] and lora_up = L2^T
+ *    as [N][rank], i.e. the weights of the two small linears K->rank and
+ *    rank->N.
+ *  - INT4 codes: two's-complement nibbles in [-7, 7], code k in the low
+ *    nibble of byte k/2 when k is even; rows of K/2 bytes.
+ *    INT4 scales: fp16, one per 64 consecutive k of a row, group-major
+ *    [K/64][rows].  MXFP4 codes: E2M1 nibbles (sign in bit 3), same packing;
+ *    MXFP4 scales: E8M0 bytes, one per 32 k, group-major [K/32][rows].
+ *  - Shapes: M, N >= 1 (any value); K >= 64 and K % 64 == 0 for INT4,
+ *    K % 128 == 0 for MXFP4; rank == 0 (no low-rank branch) or a multiple of
+ *    16, at most 256 and at most min(K, N).
+ *  - Device pointers must be 16-byte aligned.
+ *  - Errors: arguments and the device are checked before anything is
+ *    launched and reported as a status code; nothing is thrown across the
+ *    ABI.  A launch failure returns SVDQ_ERR_HIP.  A device that is not
+ *    gfx950 (or no device) gives SVDQ_ERR_UNSUPPORTED_DEVICE, never a wrong
+ *    result: the blog's "Hardware support" section has the loader check the
+ *    GPU generation and raise a clear error instead of producing wrong
+ *    outputs.
+ *  - The hot calls enqueue on `stream` (a hipStream_t; NULL = the default
+ *    stream of the current device) and never synchronize.
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define SVDQ_API __attribute__((visibility("default")))
+#else
+#define SVDQ_API
+#endif
+
+#define SVDQ_OK                       0
+#define SVDQ_ERR_INVALID_ARG         -1   /* NULL or misaligned pointer, bad enum */
+#define SVDQ_ERR_SHAPE               -2   /* M, N, K or rank outside the rules above */
+#define SVDQ_ERR_UNSUPPORTED_DEVICE  -3   /* no gfx950 device */
+#define SVDQ_ERR_HIP                 -4   /* a HIP runtime call or launch failed */
+
+#define SVDQ_INT4   0   /* int4 codes, groups of 64 along K, fp16 scales */
+#define SVDQ_MXFP4  1   /* FP4 E2M1 codes, blocks of 32 along K, E8M0 scales */
+
+/* Library version, major*10000 + minor*100 + patch. */
+SVDQ_API int svdq_version(void);
+
+/* Static text for a status code (never NULL). */
+SVDQ_API const char* svdq_status_string(int status);
+
+/* SVDQ_OK if HIP device `device` exists and is a gfx950, else
+ * SVDQ_ERR_UNSUPPORTED_DEVICE.  The answer is cached per device. */
+SVDQ_API int svdq_device_check(int device);
+
+/* Byte sizes of the packed weight buffers for (K, N, rank, precision):
+ * out_bytes[0] smooth_inv, [1] lora_down, [2] lora_up, [3] wq, [4] ws.
+ * (host) out_bytes must hold 5 entries. */
+SVDQ_API int svdq_packed_sizes(int K, int N, int rank, int precision, size_t* out_bytes);
+
+/* Byte sizes of the activation buffers for (M, K, rank, precision):
+ * out_bytes[0] xq, [1] xs, [2] lora_act.  (host) out_bytes holds 3 entries. */
+SVDQ_API int svdq_act_sizes(int M, int K, int rank, int precision, size_t* out_bytes);
+
+/* Offline pack, on the CPU (all pointers host).
+ *
+ * Stage 2 (smoothing): lambda_j = sqrt(max(act_absmax_j, 1e-5)) /
+ * sqrt(max(max_n |W[n][j]|, 1e-5)) in fp64 (migration strength 0.5; the
+ * pages give no formula) and smooth_inv_j = fp32(1/lambda_j).
+ * W^ = W / smooth_inv in fp64.  Stage 3: top-`rank` SVD of W^ =
+ * U S V^T by subspace iteration on the Gram matrix of the smaller side;
+ * L1 = bf16(fp32(U_r S_r)), L2 = bf16(fp32(V_r^T)); residual
+ * R = fp32(W^ - L1 L2) with the rounded factors; R quantized per output
+ * channel with the layer's 4-bit rule.
+ *
+ *   w_bf16      [N][K] bf16 bits        nn.Linear weight
+ *   act_absmax  [K] fp32                max |X[:, j]| of calibration data
+ *   smooth_inv  [K] fp32                out
+ *   lora_down   [rank][K] bf16          out (L1^T); may be NULL if rank == 0
+ *   lora_up     [N][rank] bf16          out (L2^T); may be NULL if rank == 0
+ *   wq          [N][K/2] uint8          out, packed codes of R
+ *   ws          [K/64][N] fp16 (INT4) or [K/32][N] uint8 E8M0 (MXFP4), out
+ *   r_out       [K][N] fp32             out, the unquantized residual; may be NULL
+ * Threads: SVDQ_NUM_THREADS, else OMP_NUM_THREADS, else the host's cores
+ * (at most 64). */
+SVDQ_API int svdq_pack_weights(const uint16_t* w_bf16, const float* act_absmax,
+                      int K, int N, int rank, int precision,
+                      float* smooth_inv, uint16_t* lora_down, uint16_t* lora_up,
+                      uint8_t* wq, void* ws, float* r_out);
+
+/* Fused kernel 1 (Nunchaku engine caption (b): the down projection and the
+ * quantizer share their input, so X is read once).
+ *
+ *   x          (dev) [M][K] bf16        activations
+ *   smooth_inv (dev) [K] fp32           from svdq_pack_weights
+ *   lora_down  (dev) [rank][K] bf16     L1^T; ignored if rank == 0
+ *   xq         (dev) [M][K/2] uint8     out, 4-bit codes of X^
+ *   xs         (dev) [K/64][M] fp16 (INT4) | [K/32][M] E8M0 (MXFP4), out
+ *   lora_act   (dev) [M][rank] fp32     out, X^ L1 (fp32 accumulation);
+ *                                       ignored if rank == 0
+ * X^ = bf16(fp32(x * smooth_inv)) is rounded once and feeds both branches.
+ * INT4 rule per 64-group of a row: s = fp16(fp32(amax/7)) (round to
+ * nearest even, saturating at 65504), s == 0 -> codes 0, else
+ * q = clamp(rint(fp32(x^ * fp32(1/s))), -7, 7), ties to even. */
+SVDQ_API int svdq_quantize_act_lora_down(const void* x, int M, int K,
+                                const float* smooth_inv, const void* lora_down,
+                                int rank, int precision,
+                                uint8_t* xq, void* xs, float* lora_act,
+                                void* stream);
+
+/* Fused kernel 2 (Nunchaku engine caption (b): the up projection and the
+ * 4-bit compute share their output, so Y is written once).
+ *
+ *   xq, xs     (dev) from svdq_quantize_act_lora_down
+ *   wq, ws     (dev) from svdq_pack_weights
+ *   lora_act   (dev) [M][rank] fp32; ignored if rank == 0
+ *   lora_up    (dev) [N][rank] bf16 (L2^T); ignored if rank == 0
+ *   bias       (dev) [N] bf16, or NULL for no bias
+ *   y          (dev) [M][N] bf16        out
+ * INT4: for every 64-group g the exact integer partial
+ * P = sum_k qx qw is scaled by s_x[m,g] s_w[n,g] into fp32 accumulators;
+ * the up projection bf16(lora_act) L2 and the bias are added in fp32 and Y
+ * is rounded to bf16 once. */
+SVDQ_API int svdq_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs,
+                           const uint8_t* wq, const void* ws,
+                           const float* lora_act, const void* lora_up,
+                           const void* bias, void* y,
+                           int M, int N, int K, int rank, int precision,
+                           void* stream);
+
+/* Test hook: the exact per-group integer partials of the INT4 GEMM for the
+ * output window rows [m0, m0+mt) x columns [n0, n0+nt), computed by the
+ * same device code as svdq_gemm_w4a4_lora_up.
+ *   out (dev) [mt][nt][K/64] int32.  mt, nt >= 1; the window must lie
+ *   inside [0, M) x [0, N). */
+SVDQ_API int svdq_debug_group_partials(const uint8_t* xq, const uint8_t* wq,
+                              int M, int N, int K,
+                              int m0, int n0, int mt, int nt,
+                              int32_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_H */

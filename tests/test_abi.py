@@ -1,0 +1,120 @@
+"""The C ABI: every symbol the header declares is exported, and arguments,
+shapes and the device are validated before anything is launched."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_diffusion_amd as bq
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "svdq.h")
+
+
+def _gpu_present():
+    import torch
+    return torch.cuda.is_available()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"SVDQ_API\s+[\w\s\*]+?\b(svdq_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_symbols()
+    for must in ("svdq_pack_weights", "svdq_quantize_act_lora_down", "svdq_gemm_w4a4_lora_up"):
+        assert must in names
+    assert set(names) == set(bq.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(bq.LIB_PATH)
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_internal_launchers_are_hidden():
+    lib = ctypes.CDLL(bq.LIB_PATH)
+    assert not hasattr(lib, "svdq_launch_gemm_w4a4_lora_up")
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4):
+        assert bq.status_string(st).startswith("svdq:")
+    assert "unknown" in bq.status_string(123)
+    assert bq.version() >= 100
+
+
+def test_sizes():
+    s = bq.packed_sizes(3072, 12288, 32)
+    assert s == (3072 * 4, 32 * 3072 * 2, 12288 * 32 * 2, 12288 * 1536, 48 * 12288 * 2)
+    s = bq.packed_sizes(3072, 12288, 32, bq.MXFP4)
+    assert s[4] == 96 * 12288
+    a = bq.act_sizes(4608, 3072, 32)
+    assert a == (4608 * 1536, 48 * 4608 * 2, 4608 * 32 * 4)
+
+
+@pytest.mark.parametrize("K,N,rank,prec,want", [
+    (100, 64, 16, bq.INT4, bq.SVDQ_ERR_SHAPE),      # K % 64
+    (0, 64, 0, bq.INT4, bq.SVDQ_ERR_SHAPE),
+    (128, 0, 0, bq.INT4, bq.SVDQ_ERR_SHAPE),
+    (128, 64, 8, bq.INT4, bq.SVDQ_ERR_SHAPE),       # rank % 16
+    (128, 64, 80, bq.INT4, bq.SVDQ_ERR_SHAPE),      # rank > min(K, N)
+    (4096, 4096, 272, bq.INT4, bq.SVDQ_ERR_SHAPE),  # rank > 256
+    (192, 64, 16, bq.MXFP4, bq.SVDQ_ERR_SHAPE),     # MXFP4 needs K % 128
+    (128, 64, 16, 7, bq.SVDQ_ERR_INVALID_ARG),
+])
+def test_shape_rules(K, N, rank, prec, want):
+    out = (ctypes.c_size_t * 5)()
+    assert bq.lib.svdq_packed_sizes(K, N, rank, prec, out) == want
+
+
+FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced (validation fails first)
+MIS = ctypes.c_void_p(0x10004)       # misaligned
+
+
+def test_hot_calls_reject_null_and_misaligned():
+    L = bq.lib
+    assert L.svdq_quantize_act_lora_down(None, 16, 64, FAKE, FAKE, 16, 0, FAKE, FAKE, FAKE, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert L.svdq_quantize_act_lora_down(MIS, 16, 64, FAKE, FAKE, 16, 0, FAKE, FAKE, FAKE, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert L.svdq_quantize_act_lora_down(FAKE, 16, 64, FAKE, None, 16, 0, FAKE, FAKE, FAKE, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert L.svdq_gemm_w4a4_lora_up(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, MIS, FAKE, 16, 16, 64, 16, 0, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert L.svdq_gemm_w4a4_lora_up(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 16, 16, 64, 16, 0, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert L.svdq_debug_group_partials(FAKE, None, 16, 16, 64, 0, 0, 1, 1, FAKE, None) == bq.SVDQ_ERR_INVALID_ARG
+
+
+def test_hot_calls_reject_bad_shapes():
+    L = bq.lib
+    assert L.svdq_quantize_act_lora_down(FAKE, 0, 64, FAKE, FAKE, 16, 0, FAKE, FAKE, FAKE, None) == bq.SVDQ_ERR_SHAPE
+    assert L.svdq_quantize_act_lora_down(FAKE, 16, 96, FAKE, FAKE, 16, 0, FAKE, FAKE, FAKE, None) == bq.SVDQ_ERR_SHAPE
+    assert L.svdq_quantize_act_lora_down(FAKE, 16, 64, FAKE, FAKE, 24, 0, FAKE, FAKE, FAKE, None) == bq.SVDQ_ERR_SHAPE
+    assert L.svdq_gemm_w4a4_lora_up(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 16, 0, 64, 16, 0, None) == bq.SVDQ_ERR_SHAPE
+    assert L.svdq_gemm_w4a4_lora_up(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 16, 8, 64, 16, 0, None) == bq.SVDQ_ERR_SHAPE
+    # window outside the matrix
+    assert L.svdq_debug_group_partials(FAKE, FAKE, 16, 16, 64, 10, 0, 7, 1, FAKE, None) == bq.SVDQ_ERR_SHAPE
+
+
+@pytest.mark.skipif(_gpu_present(), reason="checks the no-device path")
+def test_no_device_gives_unsupported_device_not_a_crash():
+    L = bq.lib
+    assert L.svdq_device_check(0) == bq.SVDQ_ERR_UNSUPPORTED_DEVICE
+    assert not bq.device_check(0)
+    # fully valid arguments: the device check is what refuses
+    assert L.svdq_quantize_act_lora_down(FAKE, 16, 64, FAKE, FAKE, 16, 0, FAKE, FAKE, FAKE, None) == bq.SVDQ_ERR_UNSUPPORTED_DEVICE
+    assert L.svdq_gemm_w4a4_lora_up(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 16, 16, 64, 16, 0, None) == bq.SVDQ_ERR_UNSUPPORTED_DEVICE
+    assert L.svdq_debug_group_partials(FAKE, FAKE, 16, 16, 64, 0, 0, 1, 1, FAKE, None) == bq.SVDQ_ERR_UNSUPPORTED_DEVICE
+    with pytest.raises(bq.SvdqError) as ei:
+        bq.check(bq.SVDQ_ERR_UNSUPPORTED_DEVICE)
+    assert ei.value.status == bq.SVDQ_ERR_UNSUPPORTED_DEVICE
+    assert L.svdq_device_check(-1) == bq.SVDQ_ERR_UNSUPPORTED_DEVICE
+
+
+def test_pack_validates_on_host():
+    import numpy as np
+    w = np.zeros((64, 100), np.uint16)
+    with pytest.raises(bq.SvdqError):
+        bq.pack_weights(w, np.ones(100, np.float32), 16)
+    with pytest.raises(ValueError):
+        bq.pack_weights(np.zeros((64, 128), np.uint16), np.ones(64, np.float32), 16)

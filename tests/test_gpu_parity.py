@@ -1,0 +1,231 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: bit-exact on packed 4-bit codes, fp16 scales and per-group int32
+partials; the fp32 down projection within rtol 1e-3; Y within
+max|Y - Y_oracle| <= 1e-2 * max|Y_oracle| (bf16 output rounding)."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_diffusion_amd as bq
+import oracle as O
+from tests import _cases as C
+
+pytestmark = pytest.mark.gpu
+
+Y_TOL = 1e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def host_u16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def device_layer(case):
+    pk, r = case["pk"], case["rank"]
+    return bq.PackedLinear(
+        K=case["x"].shape[1], N=pk["wq"].shape[0], rank=r, precision=bq.INT4,
+        smooth_inv=dev(pk["smooth_inv"]),
+        lora_down=dev_bf16(pk["l1"].T) if r else None,
+        lora_up=dev_bf16(pk["l2"].T) if r else None,
+        wq=dev(pk["wq"]), ws=dev(pk["ws"]),
+        bias=None if case["bias"] is None else dev_bf16(case["bias"]))
+
+
+def assert_y_close(y_bits, ref_bits, what):
+    y = O.bf16_bits_to_f32(y_bits).astype(np.float64)
+    r = O.bf16_bits_to_f32(ref_bits).astype(np.float64)
+    err = np.max(np.abs(y - r))
+    bound = Y_TOL * np.max(np.abs(r))
+    say(f"  {what}: max|dY| = {err:.3e}  bound {bound:.3e}  "
+        f"exact-bf16 fraction {np.mean(y_bits == ref_bits):.4f}")
+    assert err <= bound
+
+
+SMALL = [
+    (256, 512, 512, 16, 0, False),    # tiny config shape, no bias
+    (300, 576, 200, 32, 1, True),     # ragged M, 9 groups (ragged K step)
+    (129, 192, 131, 48, 2, True),     # rank 48, odd N (element stores)
+    (1, 64, 1, 0, 3, True),           # single token, single channel, rank 0
+    (64, 256, 64, 64, 4, False),
+    (520, 1024, 264, 16, 5, True),
+    (40, 4096, 272, 256, 6, True),    # largest rank
+]
+
+
+def _small(p):
+    return C.small_case(*p)
+
+
+@pytest.fixture(autouse=True)
+def _require_device():
+    assert bq.device_check(0), "gfx950 device required for the GPU tests"
+
+
+@pytest.mark.parametrize("p", SMALL, ids=lambda p: "M%dK%dN%dr%d" % p[:4])
+def test_k1_parity(p):
+    case = _small(p)
+    say(f"k1 {p}")
+    pk, r = case["pk"], case["rank"]
+    layer = device_layer(case)
+    xq, xs, la = bq.quantize_act_lora_down(dev_bf16(case["x"]), layer.smooth_inv, layer.lora_down, r)
+    torch.cuda.synchronize()
+    ref = O.quantize_act_lora_down(case["x"], pk["smooth_inv"], pk["l1"])
+    assert np.array_equal(xq.cpu().numpy(), ref["xq"])
+    assert np.array_equal(host_u16(xs), ref["xs"].view(np.uint16))
+    if r:
+        t = ref["t"]
+        got = la.cpu().numpy().astype(np.float64)
+        assert np.allclose(got, t, rtol=1e-3, atol=1e-4 * np.max(np.abs(t)))
+
+
+def test_k1_quantizer_edge_values():
+    """Magnitudes across the bf16 range, exact ties, zero groups, groups
+    whose fp16 scale is subnormal, flushes to zero or saturates."""
+    rng = np.random.default_rng(99)
+    M, K = 96, 512
+    x = np.zeros((M, K), np.float32)
+    for m in range(M):
+        e = -40 + (m * 61) // M          # 2^-40 .. 2^20
+        row = rng.standard_normal(K).astype(np.float32) * np.float32(2.0 ** e)
+        if m % 5 == 1:                   # exact ties after scaling
+            row = ((rng.integers(-6, 6, K) + 0.5) * 2.0 ** (e - 3)).astype(np.float32)
+            row[::64] = np.float32(7 * 2.0 ** (e - 3))
+        if m % 7 == 2:
+            row[64:128] = 0
+        x[m] = row
+    x[3, :64] = np.float32(458752.0)     # saturating scale
+    x[4, :2] = [np.float32(7 * 2.0 ** -25), 0]   # scale ties to zero
+    xb = O.f32_to_bf16_bits(x)
+    sinv = np.ones(K, np.float32)
+    xq, xs, _ = bq.quantize_act_lora_down(dev_bf16(xb), dev(sinv), None, 0)
+    torch.cuda.synchronize()
+    ref = O.quantize_act_lora_down(xb, sinv, np.zeros((K, 0), np.uint16))
+    assert np.array_equal(xq.cpu().numpy(), ref["xq"])
+    assert np.array_equal(host_u16(xs), ref["xs"].view(np.uint16))
+
+
+@pytest.mark.parametrize("p", SMALL, ids=lambda p: "M%dK%dN%dr%d" % p[:4])
+def test_partials_exact(p):
+    case = _small(p)
+    say(f"partials {p}")
+    pk = case["pk"]
+    ref_a = O.quantize_act_lora_down(case["x"], pk["smooth_inv"], pk["l1"])
+    M, K = case["x"].shape
+    N = pk["wq"].shape[0]
+    xq, wq = dev(ref_a["xq"]), dev(pk["wq"])
+    P = bq.debug_group_partials(xq, wq, M, N, K, 0, 0, M, N)
+    torch.cuda.synchronize()
+    ref = O.group_partials(ref_a["xq"], pk["wq"])
+    assert np.array_equal(P.cpu().numpy().astype(np.int64), ref)
+    if M > 3 and N > 3:      # an interior window
+        m0, n0, mt, nt = M // 3, N // 3, max(1, M // 2), max(1, N // 2)
+        Pw = bq.debug_group_partials(xq, wq, M, N, K, m0, n0, mt, nt)
+        torch.cuda.synchronize()
+        assert np.array_equal(Pw.cpu().numpy().astype(np.int64), ref[m0:m0 + mt, n0:n0 + nt])
+
+
+@pytest.mark.parametrize("p", SMALL, ids=lambda p: "M%dK%dN%dr%d" % p[:4])
+def test_k2_parity(p):
+    case = _small(p)
+    say(f"k2 {p}")
+    pk, r = case["pk"], case["rank"]
+    M, K = case["x"].shape
+    N = pk["wq"].shape[0]
+    ref = C.oracle_rows(case, np.arange(M))
+    layer = device_layer(case)
+    la = dev(ref["t"].astype(np.float32)) if r else None
+    y = bq.gemm_w4a4_lora_up(dev(ref["xq"]), dev(ref["xs"]), layer.wq, layer.ws, la, layer.lora_up,
+                             layer.bias, M, N, K, r)
+    torch.cuda.synchronize()
+    assert_y_close(host_u16(y), ref["y"], "k2")
+
+
+@pytest.mark.parametrize("p", SMALL, ids=lambda p: "M%dK%dN%dr%d" % p[:4])
+def test_layer_end_to_end(p):
+    case = _small(p)
+    say(f"layer {p}")
+    M = case["x"].shape[0]
+    ref = C.oracle_rows(case, np.arange(M))
+    y = bq.linear(dev_bf16(case["x"]), device_layer(case))
+    torch.cuda.synchronize()
+    assert_y_close(host_u16(y), ref["y"], "layer")
+
+
+def test_outputs_reused_buffers_and_streams():
+    """Caller-owned outputs are written in place; a side stream works."""
+    case = _small(SMALL[1])
+    M = case["x"].shape[0]
+    layer = device_layer(case)
+    x = dev_bf16(case["x"])
+    ref = C.oracle_rows(case, np.arange(M))
+    y = torch.full((M, layer.N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        bq.linear(x, layer, y=y)
+    s.synchronize()
+    assert_y_close(host_u16(y), ref["y"], "stream")
+
+
+# ---------------------------------------------------------------------------
+# full FLUX sizes: whole tensors on the GPU, oracle on sampled rows
+# ---------------------------------------------------------------------------
+
+def _sample_rows(M, seed=0):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 17, 1000, 2047, 4095, 4096, M - 2, M - 1]
+    rest = rng.choice(M, 23, replace=False)
+    return np.unique(np.concatenate([fixed, rest]))
+
+
+def _full_case(name):
+    if name == "fc2":
+        return C.mlp_pair()[1]
+    return C.named_case(name)
+
+
+@pytest.mark.parametrize("name", ["qkv", "fc1", "fc1_lora", "fc2"])
+def test_full_size_layer(name):
+    say(f"full-size {name}: building oracle case")
+    case = _full_case(name)
+    pk, r = case["pk"], case["rank"]
+    M, K = case["x"].shape
+    N = pk["wq"].shape[0]
+    say(f"full-size {name}: M={M} K={K} N={N} rank={r}")
+    layer = device_layer(case)
+    x = dev_bf16(case["x"])
+    xq, xs, la = bq.quantize_act_lora_down(x, layer.smooth_inv, layer.lora_down, r)
+    y = bq.gemm_w4a4_lora_up(xq, xs, layer.wq, layer.ws, la, layer.lora_up, layer.bias, M, N, K, r)
+    torch.cuda.synchronize()
+    # first kernel on every row: exact codes and scales
+    ref_a = O.quantize_act_lora_down(case["x"], pk["smooth_inv"], pk["l1"])
+    assert np.array_equal(xq.cpu().numpy(), ref_a["xq"])
+    assert np.array_equal(host_u16(xs), ref_a["xs"].view(np.uint16))
+    t = ref_a["t"]
+    assert np.allclose(la.cpu().numpy().astype(np.float64), t, rtol=1e-3, atol=1e-4 * np.max(np.abs(t)))
+    # exact partials on windows, including the ragged corner
+    for (m0, n0) in [(0, 0), (M - 70, N - 70), (M // 2, N // 3)]:
+        mt, nt = 64, 64
+        P = bq.debug_group_partials(xq, layer.wq, M, N, K, m0, n0, mt, nt)
+        torch.cuda.synchronize()
+        refP = O.group_partials(ref_a["xq"][m0:m0 + mt], pk["wq"][n0:n0 + nt])
+        assert np.array_equal(P.cpu().numpy().astype(np.int64), refP)
+    # Y on sampled rows
+    rows = _sample_rows(M)
+    ref = C.oracle_rows(case, rows)
+    assert_y_close(host_u16(y)[rows], ref["y"], f"{name} end to end")

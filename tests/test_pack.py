@@ -1,0 +1,110 @@
+"""The library's offline pack (C++) against the oracle.
+
+What is unique is compared exactly: smooth_inv, and at rank 0 (no SVD) the
+packed codes and scales.  With a low-rank branch the SVD factors are not
+unique, so the product L1 L2 is checked through its singular values and the
+residual norm, and the rest through invariants (L1 L2 + R = W^, the codes
+are a valid 4-bit quantization of R)."""
+
+import numpy as np
+import pytest
+
+import bit_quantized_diffusion_amd as bq
+import oracle as O
+import synth
+
+
+def _absmax(x_bits):
+    return np.abs(O.bf16_bits_to_f32(x_bits)).max(axis=0).astype(np.float32)
+
+
+def _layer(spec):
+    lay = synth.gen_layer(spec)
+    return lay, _absmax(lay["x"])
+
+
+@pytest.mark.parametrize("spec", [
+    synth.layer_spec("tiny"),
+    synth.custom_spec(64, 448, 200, 0, seed=3),
+    synth.custom_spec(64, 1024, 96, 0, seed=4),
+], ids=lambda s: s.name)
+def test_rank0_pack_bit_exact(spec):
+    lay, ax = _layer(spec)
+    ref = O.pack_weights(lay["w"], ax, 0)
+    got = bq.pack_weights(lay["w"], ax, 0, want_residual=True)
+    assert np.array_equal(got["smooth_inv"].view(np.uint32), ref["smooth_inv"].view(np.uint32))
+    assert np.array_equal(got["r"].view(np.uint32), ref["r"].view(np.uint32))
+    assert np.array_equal(got["wq"], ref["wq"])
+    assert np.array_equal(got["ws"].view(np.uint16), ref["ws"].view(np.uint16))
+
+
+def test_rank0_mxfp4_pack_bit_exact():
+    spec = synth.custom_spec(64, 512, 160, 0, seed=5)
+    lay, ax = _layer(spec)
+    ref = O.mx_pack_weights(lay["w"], ax, 0)
+    got = bq.pack_weights(lay["w"], ax, 0, precision=bq.MXFP4)
+    assert np.array_equal(got["wq"], ref["wq"])
+    assert np.array_equal(got["ws"], ref["ws"])
+
+
+def _check_low_rank(spec, lay, ax, got, ref, tol_sig=2e-3, tol_res=1e-3):
+    r = spec.rank
+    # smoothing is exact
+    assert np.array_equal(got["smooth_inv"].view(np.uint32), ref["smooth_inv"].view(np.uint32))
+    l1 = O.bf16_bits_to_f32(got["lora_down"]).astype(np.float64).T      # K x r
+    l2 = O.bf16_bits_to_f32(got["lora_up"]).astype(np.float64).T        # r x N
+    low = l1 @ l2
+    wh = ref["w_hat"]
+    # singular values of the library's low-rank product match the top-r of W^
+    s_low = np.linalg.svd(low, compute_uv=False)[:r]
+    assert np.allclose(s_low, ref["sigma"][:r], rtol=tol_sig)
+    # Eckart-Young: the residual is as small as the oracle's
+    res_lib = np.linalg.norm(wh - low)
+    res_ref = np.linalg.norm(ref["r"].astype(np.float64))
+    assert abs(res_lib - res_ref) <= tol_res * res_ref
+    # L1 L2 + R = W^ to fp32 rounding of R
+    R = got["r"].astype(np.float64)
+    ulp = np.spacing(np.abs(got["r"])).astype(np.float64)
+    assert np.all(np.abs(low + R - wh) <= ulp)
+    # rows of L2 are orthonormal up to bf16 rounding
+    assert np.allclose(l2 @ l2.T, np.eye(r), atol=2e-2)
+    # the codes are a valid 4-bit quantization of R: |R - s q| <= s/2 for
+    # normal fp16 scales, and s is amax/7 rounded to fp16
+    K, N = R.shape
+    q = O.unpack_int4(got["wq"]).astype(np.float64)                     # N x K
+    s = got["ws"].astype(np.float64)                                     # G x N
+    sfull = np.repeat(s.T, 64, axis=1)                                   # N x K
+    err = np.abs(R.T - q * sfull)
+    normal = sfull >= 2.0 ** -14
+    assert np.all(err[normal] <= 0.5 * sfull[normal] * (1 + 2e-3))
+    amax = np.abs(R.T.reshape(N, K // 64, 64)).max(axis=2)
+    assert np.allclose(s.T, amax / 7, rtol=2.0 ** -10, atol=2.0 ** -24)
+
+
+@pytest.mark.parametrize("spec", [
+    synth.layer_spec("tiny"),                                   # K <= N: Gram over K
+    synth.custom_spec(96, 512, 128, 16, seed=6),                # K > N: Gram over N
+    synth.custom_spec(96, 256, 320, 48, seed=7),                # rank 48
+], ids=lambda s: s.name)
+def test_low_rank_pack_against_oracle(spec):
+    lay, ax = _layer(spec)
+    ref = O.pack_weights(lay["w"], ax, spec.rank)
+    got = bq.pack_weights(lay["w"], ax, spec.rank, want_residual=True)
+    _check_low_rank(spec, lay, ax, got, ref)
+
+
+def test_full_rank_pack_reconstructs():
+    spec = synth.custom_spec(32, 128, 64, 64, seed=8)
+    lay, ax = _layer(spec)
+    got = bq.pack_weights(lay["w"], ax, 64, want_residual=True)
+    ref = O.pack_weights(lay["w"], ax, 64)
+    assert np.linalg.norm(got["r"]) <= 1e-2 * np.linalg.norm(ref["w_hat"])
+
+
+def test_pack_is_deterministic():
+    spec = synth.custom_spec(32, 256, 128, 32, seed=9)
+    lay, ax = _layer(spec)
+    a = bq.pack_weights(lay["w"], ax, 32)
+    b = bq.pack_weights(lay["w"], ax, 32)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
