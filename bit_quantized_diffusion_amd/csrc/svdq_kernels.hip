@@ -23,7 +23,10 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------
 // number formats on the device
@@ -35,8 +38,11 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-__device__ __forceinline__ float bf16_round(float f) {
-  return __uint_as_float(bf16_rne_bits(f) << 16);
+// two fp32 -> packed bf16 pair (lo, hi), round to nearest even
+// (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const v2bf b = __builtin_convertvector((v2f{lo, hi}), v2bf);
+  return __builtin_bit_cast(uint32_t, b);
 }
 
 // fp32 -> fp16 bits with round to nearest even; finite values saturate to
@@ -52,12 +58,7 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
 }
 
-// two bf16 values that are exact in fp32 -> one packed dword (lo, hi)
-__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
-  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
-
-// fp32 -> packed bf16 pair with round to nearest even
+// fp32 -> packed bf16 pair with round to nearest even (bit arithmetic)
 __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
   return bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
 }
@@ -65,106 +66,109 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
 // ---------------------------------------------------------------------------
 // Kernel 1: smoothing + INT4 activation quantization + down projection.
 //
-// One workgroup = 4 waves over 16 rows and all of K.  A wave step covers the
-// 16 rows x 4 groups of 64 k; lane l owns row l % 16 and group l / 16 of the
-// step, so the group's absmax, scale and codes are lane-local.  The same
-// bf16 X^ registers feed the bf16 MFMA with L1 (8 MFMAs of K = 32 per step
-// and rank tile).  Waves take steps round-robin; their partial X^ L1 tiles
-// are summed in LDS at the end (a fixed order, so the result is
-// deterministic).
+// A workgroup owns 16 rows and all of K, with W waves (W = blockDim/64).  A
+// wave step covers the 16 rows x 2 groups (128 k): lane l owns row l % 16
+// and, for chunk c = 0..3 of 32 k, the 8 k at c*32 + (l/16)*8, so every
+// load instruction reads 64 contiguous bytes of each of 16 rows.  The group
+// absmax is combined over the 4 lanes of a row with two lane exchanges.  X^
+// is rounded to bf16 by v_cvt_pk_bf16_f32; the packed pairs are the A
+// operand of the bf16 MFMA with L1 (K = 32 per chunk), so X is read once.
+// Waves take steps round-robin and their partial X^ L1 tiles are summed in
+// LDS in a fixed order (deterministic).
 // ---------------------------------------------------------------------------
 
 template <int RT>
-__global__ __launch_bounds__(256) void k1_quant_down_int4(
+__global__ __launch_bounds__(512) void k1_quant_down_int4(
     const uint16_t* __restrict__ x, int M, int K, const float* __restrict__ sinv,
     const uint16_t* __restrict__ ldown, uint8_t* __restrict__ xq, uint16_t* __restrict__ xs,
     float* __restrict__ lact) {
   constexpr int RANK = RT * 16;
-  __shared__ float red[RT > 0 ? 4 * 16 * RANK : 1];
+  extern __shared__ float red[];            // [W][16][RANK]
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int W = blockDim.x >> 6;
   const int r16 = lane & 15;
   const int q = lane >> 4;
   const int row0 = blockIdx.x * 16;
   const int row = row0 + r16;
   const bool row_ok = row < M;
   const int G = K / 64;
-  const int nsteps = (G + 3) / 4;
+  const int nsteps = (G + 1) / 2;
+  const size_t xrow = static_cast<size_t>(row) * K;
 
   v4f acc[RT > 0 ? RT : 1];
 #pragma unroll
   for (int t = 0; t < (RT > 0 ? RT : 1); ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int step = wave; step < nsteps; step += 4) {
-    const int g = step * 4 + q;
-    const bool g_ok = g < G;
-    const bool ok = row_ok && g_ok;
-    const int k0 = g * 64;
-    float v[64];
-    if (ok) {
-      const uint4* src = reinterpret_cast<const uint4*>(x + static_cast<size_t>(row) * K + k0);
-      const float4* sp = reinterpret_cast<const float4*>(sinv + k0);
+  for (int step = wave; step < nsteps; step += W) {
+    const int kbase = step * 128;
+    float xh[4][8];
+    uint32_t pk[4][4];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const uint4 w = src[c];
-        const float4 s0 = sp[2 * c], s1 = sp[2 * c + 1];
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-        const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float lo = __uint_as_float(ws[e] << 16);
-          const float hi = __uint_as_float(ws[e] & 0xFFFF0000u);
-          v[8 * c + 2 * e] = bf16_round(lo * ss[2 * e]);
-          v[8 * c + 2 * e + 1] = bf16_round(hi * ss[2 * e + 1]);
-        }
+    for (int c = 0; c < 4; ++c) {
+      const int kc = kbase + c * 32 + q * 8;
+      const bool valid = kbase + c * 32 < K;
+      uint4 w = make_uint4(0, 0, 0, 0);
+      float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
+      if (valid) {
+        if (row_ok) w = *reinterpret_cast<const uint4*>(x + xrow + kc);
+        s0 = *reinterpret_cast<const float4*>(sinv + kc);
+        s1 = *reinterpret_cast<const float4*>(sinv + kc + 4);
       }
-    } else {
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+      const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-      for (int i = 0; i < 64; ++i) v[i] = 0.f;
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __uint_as_float(ws[e] << 16) * ss[2 * e];
+        const float hi = __uint_as_float(ws[e] & 0xFFFF0000u) * ss[2 * e + 1];
+        const uint32_t p = cvt_pk_bf16(lo, hi);
+        pk[c][e] = p;
+        xh[c][2 * e] = __uint_as_float(p << 16);
+        xh[c][2 * e + 1] = __uint_as_float(p & 0xFFFF0000u);
+      }
     }
 
-    // per-group absmax -> fp16 scale -> codes
-    float amax = 0.f;
+    // two groups per step: chunks {0,1} and {2,3}
 #pragma unroll
-    for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    const uint32_t sbits = f16_sat_bits(__fdiv_rn(amax, 7.0f));
-    const float s = f16_bits_to_f32(sbits);
-    const float inv = (s == 0.f) ? 0.f : __fdiv_rn(1.0f, s);
-    uint32_t packed[8];
+    for (int j = 0; j < 2; ++j) {
+      const int g = step * 2 + j;
+      float amax = 0.f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      uint32_t word = 0;
+      for (int c = 2 * j; c < 2 * j + 2; ++c)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float qf = __builtin_rintf(v[8 * c + e] * inv);
-        qf = fminf(7.f, fmaxf(-7.f, qf));
-        const int qi = static_cast<int>(qf);
-        word |= (static_cast<uint32_t>(qi) & 0xFu) << (4 * e);
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(xh[c][e]));
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      const uint32_t sbits = f16_sat_bits(__fdiv_rn(amax, 7.0f));
+      const float s = f16_bits_to_f32(sbits);
+      const float inv = (s == 0.f) ? 0.f : __fdiv_rn(1.0f, s);
+      const bool g_ok = g < G;
+#pragma unroll
+      for (int c = 2 * j; c < 2 * j + 2; ++c) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float qf = __builtin_rintf(xh[c][e] * inv);
+          qf = fminf(7.f, fmaxf(-7.f, qf));
+          word |= (static_cast<uint32_t>(static_cast<int>(qf)) & 0xFu) << (4 * e);
+        }
+        if (row_ok && g_ok)
+          *reinterpret_cast<uint32_t*>(xq + xrow / 2 + (kbase + c * 32 + q * 8) / 2) = word;
       }
-      packed[c] = word;
-    }
-    if (ok) {
-      uint4* dst = reinterpret_cast<uint4*>(xq + static_cast<size_t>(row) * (K / 2) + k0 / 2);
-      dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-      dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-      xs[static_cast<size_t>(g) * M + row] = static_cast<uint16_t>(sbits);
+      if (row_ok && g_ok && q == j) xs[static_cast<size_t>(g) * M + row] = static_cast<uint16_t>(sbits);
     }
 
     if constexpr (RT > 0) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        v4i araw;
-        araw.x = static_cast<int>(pack_bf16_exact(v[8 * j + 0], v[8 * j + 1]));
-        araw.y = static_cast<int>(pack_bf16_exact(v[8 * j + 2], v[8 * j + 3]));
-        araw.z = static_cast<int>(pack_bf16_exact(v[8 * j + 4], v[8 * j + 5]));
-        araw.w = static_cast<int>(pack_bf16_exact(v[8 * j + 6], v[8 * j + 7]));
-        const v8bf a = __builtin_bit_cast(v8bf, araw);
+      for (int c = 0; c < 4; ++c) {
+        const int kc = kbase + c * 32 + q * 8;
+        const bool valid = kbase + c * 32 < K;
+        const v8bf a = __builtin_bit_cast(v8bf, (v4i{static_cast<int>(pk[c][0]), static_cast<int>(pk[c][1]),
+                                                     static_cast<int>(pk[c][2]), static_cast<int>(pk[c][3])}));
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
           v4i braw = v4i{0, 0, 0, 0};
-          if (g_ok) {
-            braw = *reinterpret_cast<const v4i*>(ldown + static_cast<size_t>(t * 16 + r16) * K + k0 + 8 * j);
-          }
+          if (valid) braw = *reinterpret_cast<const v4i*>(ldown + static_cast<size_t>(t * 16 + r16) * K + kc);
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, braw), acc[t], 0, 0, 0);
         }
       }
@@ -177,9 +181,10 @@ __global__ __launch_bounds__(256) void k1_quant_down_int4(
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[(wave * 16 + 4 * q + i) * RANK + t * 16 + r16] = acc[t][i];
     __syncthreads();
-    for (int e = threadIdx.x; e < 16 * RANK; e += 256) {
+    for (int e = threadIdx.x; e < 16 * RANK; e += blockDim.x) {
       const int rr = e / RANK;
-      const float sum = ((red[e] + red[16 * RANK + e]) + red[2 * 16 * RANK + e]) + red[3 * 16 * RANK + e];
+      float sum = red[e];
+      for (int w2 = 1; w2 < W; ++w2) sum += red[w2 * 16 * RANK + e];
       if (row0 + rr < M) lact[static_cast<size_t>(row0 + rr) * RANK + (e - rr * RANK)] = sum;
     }
   }
@@ -188,24 +193,36 @@ __global__ __launch_bounds__(256) void k1_quant_down_int4(
 // ---------------------------------------------------------------------------
 // Kernel 2: INT4 GEMM + per-group dequant + up projection + bias.
 //
-// Output tile 128 (n) x 128 (m) per workgroup of 4 waves; each wave owns a
-// 64 x 64 sub-tile = 4 x 4 MFMA tiles.  The MFMA computes Y^T tiles (A = W
-// codes, B = X codes) so that a lane ends up with 4 consecutive output
-// channels of one token, which it stores as one 8-byte write.
+// Output tile 128 (n) x 128 (m) per workgroup of 8 waves; each wave owns a
+// 64 (n) x 32 (m) sub-tile = 4 x 2 MFMA tiles.  The MFMA computes Y^T tiles
+// (A = W codes, B = X codes) so that a lane ends up with 4 consecutive
+// output channels of one token, which it stores as one 8-byte write.  The
+// register budget is 128 VGPRs so that two workgroups (16 waves) share a CU
+// and hide memory latency.
 //
-// Per K-group of 64: the packed int4 tiles are read from global memory
-// (16 B per thread per operand), unpacked to int8 with the x16 nibble trick
+// Per K-group of 64: every thread loads 16 packed bytes of one operand tile
+// from global memory two groups before they are needed (two register sets
+// used alternately), unpacks them to int8 with the x16 nibble trick
 // ((w << 4) & 0xF0F0F0F0 holds 16*q of the even codes, w & 0xF0F0F0F0 16*q
-// of the odd codes, both exact int8), written to LDS (double buffered) and
-// fed to v_mfma_i32_16x16x64_i8.  Each MFMA returns 256 * P for the group,
-// an exact int32; the 1/256 is folded into the activation scale, and the
-// fp32 accumulator gets fma(float(256 P), s_w * s_x / 256, acc).  After the
-// K loop the bf16 up projection runs on the same accumulators (MFMA srcC),
-// then the bias is added and Y is rounded to bf16 and stored once.
+// of the odd codes, both exact int8) and stores them into a three-slot LDS
+// ring (iteration g reads slot g%3 while g+2 is stored into slot (g+2)%3,
+// whose last readers passed the previous barrier; one barrier per group).
+// v_mfma_i32_16x16x64_i8 returns 256*P for the group, an exact int32.  The
+// dequant factor s_w[n] s_x[m] of every output element comes from a second,
+// exact matrix-core product: an f16 MFMA whose only non-zero k-slot holds
+// s_w (A) and s_x (B), so S[n][m] = s_w s_x exactly in fp32 and in the same
+// lane layout as P.  The scales sit in LDS as ready-made operands
+// (s, 0, 0, 0) so one 16-byte read fills an operand.  That leaves two VALU
+// operations per output element and group (convert, fma) instead of three:
+// on gfx950 the per-group dequant on the VALU, not the MFMA, bounds this
+// kernel.  After the K loop the 1/256 is applied, the bf16 up projection
+// runs on the same accumulators (MFMA srcC), the bias is added and Y is
+// rounded to bf16 and stored once.
 // ---------------------------------------------------------------------------
 
 constexpr int kTile = 128;      // output tile edge (both n and m)
 constexpr int kLdsRow = 80;     // 64 bytes of int8 codes + 16 bytes padding
+constexpr int kK2Threads = 512;
 
 struct TileCoord {
   int n0, m0;
@@ -246,28 +263,28 @@ __device__ __forceinline__ void unpack_store(int8_t* dst, const uint4& w) {
 }
 
 template <bool DEBUG>
-__global__ __launch_bounds__(256, 2) void k2_gemm_int4(
+__global__ __launch_bounds__(kK2Threads, 4) void k2_gemm_int4(
     const uint8_t* __restrict__ xq, const uint16_t* __restrict__ xs,
     const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
     const float* __restrict__ lact, const uint16_t* __restrict__ lup,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
     int M, int N, int K, int rank,
     int win_m0, int win_n0, int win_mt, int win_nt, int32_t* __restrict__ dbg) {
-  __shared__ __attribute__((aligned(16))) int8_t lds_w[2][kTile * kLdsRow];
-  __shared__ __attribute__((aligned(16))) int8_t lds_x[2][kTile * kLdsRow];
-  __shared__ __attribute__((aligned(16))) float lds_sw[2][kTile];
-  __shared__ __attribute__((aligned(16))) float lds_sx[2][kTile];
+  __shared__ __attribute__((aligned(16))) int8_t lds_w[3][kTile * kLdsRow];
+  __shared__ __attribute__((aligned(16))) int8_t lds_x[3][kTile * kLdsRow];
+  __shared__ __attribute__((aligned(16))) float lds_sw[DEBUG ? 1 : 3][kTile];
+  __shared__ float lds_sx[DEBUG ? 1 : 3][kTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int r16 = lane & 15;
   const int q = lane >> 4;
-  const int wn = wave >> 1, wm = wave & 1;
+  const int wn = wave >> 2, wm = wave & 3;     // 2 x 4 waves: 64 n x 32 m each
   const int G = K / 64;
   const size_t rowb = static_cast<size_t>(K / 2);
 
-  int n0, m0, row_lim_n, row_lim_m;
+  int n0, m0;
   if constexpr (DEBUG) {
     const int tiles_m = (win_mt + kTile - 1) / kTile;
     n0 = win_n0 + (blockIdx.x / tiles_m) * kTile;
@@ -277,70 +294,75 @@ __global__ __launch_bounds__(256, 2) void k2_gemm_int4(
     n0 = tc.n0;
     m0 = tc.m0;
   }
-  row_lim_n = N;
-  row_lim_m = M;
 
-  // loader role: thread t moves 16 packed bytes of row t/2, half t%2
-  const int lrow = tid >> 1, lhalf = tid & 1;
-  const bool w_ok = n0 + lrow < row_lim_n;
-  const bool x_ok = m0 + lrow < row_lim_m;
-  const uint8_t* wsrc = wq + static_cast<size_t>(n0 + lrow) * rowb + lhalf * 16;
-  const uint8_t* xsrc = xq + static_cast<size_t>(m0 + lrow) * rowb + lhalf * 16;
+  // loader role: threads 0..255 move 16 packed bytes of W row t/2 (half t%2),
+  // threads 256..511 the same for X
+  const bool ld_is_w = tid < 256;
+  const int lt = tid & 255;
+  const int lrow = lt >> 1, lhalf = lt & 1;
+  const bool ld_ok = ld_is_w ? (n0 + lrow < N) : (m0 + lrow < M);
+  const uint8_t* ldsrc = (ld_is_w ? wq + static_cast<size_t>(n0 + lrow) * rowb
+                                  : xq + static_cast<size_t>(m0 + lrow) * rowb) + lhalf * 16;
+  int8_t* const lddst0 = (ld_is_w ? &lds_w[0][0] : &lds_x[0][0]) + lrow * kLdsRow + lhalf * 32;
   // scale role: threads 0..127 move s_w of row n0+t, 128..255 s_x of m0+t-128
+  const bool sc_thread = !DEBUG && tid < 2 * kTile;
   const bool sc_is_w = tid < kTile;
-  const int sc_i = sc_is_w ? tid : tid - kTile;
-  const bool sc_ok = sc_is_w ? (n0 + sc_i < N) : (m0 + sc_i < M);
-  const uint16_t* scsrc = sc_is_w ? (ws + n0 + sc_i) : (xs + m0 + sc_i);
+  const int sc_i = tid & (kTile - 1);
+  const bool sc_ok = sc_thread && (sc_is_w ? (n0 + sc_i < N) : (m0 + sc_i < M));
+  const uint16_t* scsrc = DEBUG ? nullptr : (sc_is_w ? (ws + n0 + sc_i) : (xs + m0 + sc_i));
   const size_t sc_stride = sc_is_w ? static_cast<size_t>(N) : static_cast<size_t>(M);
 
-  uint4 wreg = make_uint4(0, 0, 0, 0), xreg = make_uint4(0, 0, 0, 0);
-  float screg = 0.f;
-  auto gload = [&](int g) {
-    wreg = w_ok ? *reinterpret_cast<const uint4*>(wsrc + g * 32) : make_uint4(0, 0, 0, 0);
-    xreg = x_ok ? *reinterpret_cast<const uint4*>(xsrc + g * 32) : make_uint4(0, 0, 0, 0);
-    if constexpr (!DEBUG) screg = sc_ok ? f16_bits_to_f32(scsrc[static_cast<size_t>(g) * sc_stride]) : 0.f;
+  struct LoadRegs {
+    uint4 c;
+    uint32_t sc;
   };
-  auto lstore = [&](int buf) {
-    unpack_store(&lds_w[buf][lrow * kLdsRow + lhalf * 32], wreg);
-    unpack_store(&lds_x[buf][lrow * kLdsRow + lhalf * 32], xreg);
-    if (sc_is_w) lds_sw[buf][sc_i] = screg;
-    else lds_sx[buf][sc_i] = screg * 0.00390625f;   // 1/256, exact
+  auto gload = [&](int g, LoadRegs& L) {
+    L.c = ld_ok ? *reinterpret_cast<const uint4*>(ldsrc + g * 32) : make_uint4(0, 0, 0, 0);
+    if constexpr (!DEBUG) L.sc = sc_ok ? static_cast<uint32_t>(scsrc[static_cast<size_t>(g) * sc_stride]) : 0u;
+  };
+  auto lstore = [&](int g, const LoadRegs& L) {
+    const int buf = g % 3;
+    unpack_store(lddst0 + buf * (kTile * kLdsRow), L.c);
+    if constexpr (!DEBUG) {
+      if (sc_thread) {
+        // s_x carries the 1/256 of the x16 nibble trick (exact)
+        const float v = f16_bits_to_f32(L.sc) * (sc_is_w ? 1.0f : 0.00390625f);
+        float* dst = sc_is_w ? &lds_sw[buf][sc_i] : &lds_sx[buf][sc_i];
+        *dst = v;
+      }
+    }
   };
 
-  v4f acc[4][4];
+  v4f acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    if (g + 1 < G) gload(g + 1);
-
-    v4i a[4], b[4];
-    v4f sw4[4];
-    float sx1[4];
+  auto compute = [&](int g) {
+    const int buf = g % 3;
+    v4i a[4], b[2];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int it = 0; it < 4; ++it)
       a[it] = *reinterpret_cast<const v4i*>(&lds_w[buf][(wn * 64 + it * 16 + r16) * kLdsRow + q * 16]);
-      sw4[it] = *reinterpret_cast<const v4f*>(&lds_sw[buf][wn * 64 + it * 16 + 4 * q]);
-    }
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      b[jt] = *reinterpret_cast<const v4i*>(&lds_x[buf][(wm * 64 + jt * 16 + r16) * kLdsRow + q * 16]);
-      sx1[jt] = lds_sx[buf][wm * 64 + jt * 16 + r16];
+    for (int jt = 0; jt < 2; ++jt)
+      b[jt] = *reinterpret_cast<const v4i*>(&lds_x[buf][(wm * 32 + jt * 16 + r16) * kLdsRow + q * 16]);
+    v4f sw4[4];
+    float sx1[2];
+    if constexpr (!DEBUG) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) sw4[it] = *reinterpret_cast<const v4f*>(&lds_sw[buf][wn * 64 + it * 16 + 4 * q]);
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) sx1[jt] = lds_sx[buf][wm * 32 + jt * 16 + r16];
     }
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
+      for (int jt = 0; jt < 2; ++jt) {
         const v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[it], b[jt], v4i{0, 0, 0, 0}, 0, 0, 0);
         if constexpr (DEBUG) {
-          const int m = m0 + wm * 64 + jt * 16 + r16;
+          const int m = m0 + wm * 32 + jt * 16 + r16;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int n = n0 + wn * 64 + it * 16 + 4 * q + i;
@@ -350,14 +372,34 @@ __global__ __launch_bounds__(256, 2) void k2_gemm_int4(
           }
         } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float s = sw4[it][i] * sx1[jt];
-            acc[it][jt][i] = __builtin_fmaf(static_cast<float>(p[i]), s, acc[it][jt][i]);
-          }
+          for (int i = 0; i < 4; ++i)
+            acc[it][jt][i] = __builtin_fmaf(static_cast<float>(p[i]), sw4[it][i] * sx1[jt], acc[it][jt][i]);
         }
       }
+      // one row tile's products in flight at a time (register budget)
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (g + 1 < G) lstore(buf ^ 1);
+  };
+
+  // prologue: groups 0 and 1 into LDS
+  LoadRegs ld;
+  ld.c = make_uint4(0, 0, 0, 0);
+  ld.sc = 0;
+  gload(0, ld);
+  lstore(0, ld);
+  if (G > 1) {
+    gload(1, ld);
+    lstore(1, ld);
+  }
+  __syncthreads();
+
+  // iteration g: issue the loads of g+2, compute g from LDS, store g+2 into
+  // the third slot, barrier.  Waves of the other workgroup on the CU run
+  // while this one waits for its loads.
+  for (int g = 0; g < G; ++g) {
+    if (g + 2 < G) gload(g + 2, ld);
+    compute(g);
+    if (g + 2 < G) lstore(g + 2, ld);
     __syncthreads();
   }
 
@@ -366,7 +408,7 @@ __global__ __launch_bounds__(256, 2) void k2_gemm_int4(
     for (int c0 = 0; c0 < rank; c0 += 32) {
       const int j = c0 + 8 * q;          // this lane's 8 k-slots
       const bool j_ok = j < rank;
-      v4i ua[4], ub[4];
+      v4i ua[4], ub[2];
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const int n = n0 + wn * 64 + it * 16 + r16;
@@ -374,8 +416,8 @@ __global__ __launch_bounds__(256, 2) void k2_gemm_int4(
                                  : v4i{0, 0, 0, 0};
       }
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        const int m = m0 + wm * 64 + jt * 16 + r16;
+      for (int jt = 0; jt < 2; ++jt) {
+        const int m = m0 + wm * 32 + jt * 16 + r16;
         if (j_ok && m < M) {
           const float4* src = reinterpret_cast<const float4*>(lact + static_cast<size_t>(m) * rank + j);
           const float4 f0 = src[0], f1 = src[1];
@@ -388,7 +430,7 @@ __global__ __launch_bounds__(256, 2) void k2_gemm_int4(
 #pragma unroll
       for (int it = 0; it < 4; ++it)
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
+        for (int jt = 0; jt < 2; ++jt)
           acc[it][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, ua[it]),
                                                                __builtin_bit_cast(v8bf, ub[jt]), acc[it][jt], 0, 0, 0);
     }
@@ -404,8 +446,8 @@ __global__ __launch_bounds__(256, 2) void k2_gemm_int4(
           if (nb + i < N) bv[i] = __uint_as_float(static_cast<uint32_t>(bias[nb + i]) << 16);
       }
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        const int m = m0 + wm * 64 + jt * 16 + r16;
+      for (int jt = 0; jt < 2; ++jt) {
+        const int m = m0 + wm * 32 + jt * 16 + r16;
         if (m >= M) continue;
         uint16_t* dst = y + static_cast<size_t>(m) * N + nb;
         const uint32_t h0 = bf16_rne_bits(acc[it][jt][0] + bv[0]);
@@ -428,8 +470,17 @@ __global__ __launch_bounds__(256, 2) void k2_gemm_int4(
 template <int RT>
 hipError_t launch_k1(const void* x, int M, int K, const float* sinv, const void* ldown, uint8_t* xq, void* xs,
                      float* lact, hipStream_t st) {
-  dim3 grid((M + 15) / 16), block(256);
-  hipLaunchKernelGGL(k1_quant_down_int4<RT>, grid, block, 0, st, static_cast<const uint16_t*>(x), M, K, sinv,
+  const int G = K / 64;
+  const int nsteps = (G + 1) / 2;
+  int waves = nsteps < 8 ? nsteps : 8;
+  if (RT > 0) {
+    const int lds_cap = 1024 / (RT * 16);     // W * 16 * RANK * 4 bytes <= 64 KiB
+    if (waves > lds_cap) waves = lds_cap;
+  }
+  if (waves < 1) waves = 1;
+  const size_t lds = RT > 0 ? static_cast<size_t>(waves) * 16 * RT * 16 * sizeof(float) : 0;
+  dim3 grid((M + 15) / 16), block(64 * waves);
+  hipLaunchKernelGGL(k1_quant_down_int4<RT>, grid, block, lds, st, static_cast<const uint16_t*>(x), M, K, sinv,
                      static_cast<const uint16_t*>(ldown), xq, static_cast<uint16_t*>(xs), lact);
   return hipGetLastError();
 }
@@ -462,7 +513,7 @@ extern "C" int svdq_launch_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs, 
                                              int M, int N, int K, int rank, int precision, void* stream) {
   if (precision != SVDQ_INT4) return static_cast<int>(hipErrorInvalidValue);
   const int tiles = ((N + kTile - 1) / kTile) * ((M + kTile - 1) / kTile);
-  hipLaunchKernelGGL(k2_gemm_int4<false>, dim3(tiles), dim3(256), 0, static_cast<hipStream_t>(stream), xq,
+  hipLaunchKernelGGL(k2_gemm_int4<false>, dim3(tiles), dim3(kK2Threads), 0, static_cast<hipStream_t>(stream), xq,
                      static_cast<const uint16_t*>(xs), wq, static_cast<const uint16_t*>(ws), lora_act,
                      static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias),
                      static_cast<uint16_t*>(y), M, N, K, rank, 0, 0, 0, 0, nullptr);
@@ -472,7 +523,7 @@ extern "C" int svdq_launch_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs, 
 extern "C" int svdq_launch_debug_group_partials(const uint8_t* xq, const uint8_t* wq, int M, int N, int K, int m0,
                                                 int n0, int mt, int nt, int32_t* out, void* stream) {
   const int tiles = ((nt + kTile - 1) / kTile) * ((mt + kTile - 1) / kTile);
-  hipLaunchKernelGGL(k2_gemm_int4<true>, dim3(tiles), dim3(256), 0, static_cast<hipStream_t>(stream), xq, nullptr,
+  hipLaunchKernelGGL(k2_gemm_int4<true>, dim3(tiles), dim3(kK2Threads), 0, static_cast<hipStream_t>(stream), xq, nullptr,
                      wq, nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, 0, m0, n0, mt, nt, out);
   return static_cast<int>(hipGetLastError());
 }
