@@ -36,8 +36,10 @@ both this oracle and the GPU path):
       s = fp16(fp32(amax / 7)) with round-to-nearest-even and saturation at
       65504; s == 0 -> all codes 0; otherwise inv = fp32(1/s) and
       q = clamp(rint(fp32(v * inv)), -7, 7), ties to even.
-  R6  codes are two's-complement nibbles, low nibble = even k, row-major
-      [rows][K/2]; scales are group-major [K/64][rows].
+  R6  codes are sign-magnitude nibbles (bit 3 = sign, bits 0-2 = |q|; zero
+      is stored as 0), low nibble = even k, row-major [rows][K/2]; scales
+      are group-major [K/64][rows].  Sign-magnitude holds exactly the
+      symmetric range [-7, 7] of the quantizer.
   R7  x^ = bf16(fp32(x * smooth_inv)), rounded once and used by both branches.
   R8  down projection t = X^ L1 in fp64 (the GPU keeps it in fp32 [M][r]);
       the up projection uses bf16(fp32(t)).
@@ -128,22 +130,21 @@ def quantize_groups(v):
 
 
 def pack_int4(q) -> np.ndarray:
-    """int8 codes [rows][K] -> uint8 [rows][K/2]; two's-complement nibbles,
-    code k in the low nibble of byte k/2 when k is even."""
-    q = np.asarray(q)
-    u = (q.astype(np.int16) & 0xF).astype(np.uint8)
+    """int8 codes [rows][K] in [-7, 7] -> uint8 [rows][K/2] (reading R6):
+    sign-magnitude nibbles, code k in the low nibble of byte k/2 when k is
+    even."""
+    q = np.asarray(q).astype(np.int16)
+    assert np.all(np.abs(q) <= 7), "sign-magnitude nibbles hold [-7, 7]"
+    u = np.where(q < 0, 8 | (-q), q).astype(np.uint8)
     return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
 
 
 def unpack_int4(p) -> np.ndarray:
     p = np.asarray(p, dtype=np.uint8)
-    lo = (p & 0xF).astype(np.int16)
-    hi = (p >> 4).astype(np.int16)
-    lo = np.where(lo >= 8, lo - 16, lo)
-    hi = np.where(hi >= 8, hi - 16, hi)
     out = np.empty((p.shape[0], p.shape[1] * 2), dtype=np.int8)
-    out[:, 0::2] = lo
-    out[:, 1::2] = hi
+    for sl, nib in ((slice(0, None, 2), p & 0xF), (slice(1, None, 2), p >> 4)):
+        mag = (nib & 7).astype(np.int8)
+        out[:, sl] = np.where(nib & 8, -mag, mag)
     return out
 
 

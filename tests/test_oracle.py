@@ -195,12 +195,15 @@ def test_quantizer_error_bound():
 
 
 def test_pack_bytes_and_roundtrip():
-    q = np.array([[1, -1, -7, 7, 0, -8, 3, -3]], dtype=np.int8)
+    # sign-magnitude nibbles: -1 -> 0x9, -7 -> 0xF, -5 -> 0xD, -3 -> 0xB
+    q = np.array([[1, -1, -7, 7, 0, -5, 3, -3]], dtype=np.int8)
     p = O.pack_int4(q)
-    assert list(p[0]) == [0xF1, 0x79, 0x80, 0xD3]
+    assert list(p[0]) == [0x91, 0x7F, 0xD0, 0xB3]
     rng = np.random.default_rng(1)
-    q = rng.integers(-8, 8, (9, 128)).astype(np.int8)
+    q = rng.integers(-7, 8, (9, 128)).astype(np.int8)
     assert np.array_equal(O.unpack_int4(O.pack_int4(q)), q)
+    # a negative zero nibble decodes to 0
+    assert O.unpack_int4(np.array([[0x88]], np.uint8)).tolist() == [[0, 0]]
 
 
 # ---------------------------------------------------------------------------
