@@ -50,7 +50,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--sets", type=int, default=4, help="rotated buffer sets")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=24, help="token rows in the oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=96, help="token rows in the oracle sample")
     return p.parse_args()
 
 

@@ -40,6 +40,12 @@ def _load():
         raise ImportError(
             f"{LIB_PATH} is missing: build it with "
             "`python -m bit_quantized_diffusion_amd.build` (hipcc, gfx950)")
+    # The tensors handed to the library come from torch, which ships its own
+    # HIP runtime.  Load torch first so that libsvdq.so binds to that same
+    # runtime (the dynamic loader reuses the already loaded libamdhip64);
+    # loaded the other way round the process ends up with two HIP runtimes
+    # and the library's device queries fail.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)
     sig = {

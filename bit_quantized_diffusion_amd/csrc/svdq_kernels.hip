@@ -150,7 +150,9 @@ __global__ __launch_bounds__(512) void k1_quant_down_int4(
         for (int e = 0; e < 8; ++e) {
           float qf = __builtin_rintf(xh[c][e] * inv);
           qf = fminf(7.f, fmaxf(-7.f, qf));
-          word |= (static_cast<uint32_t>(static_cast<int>(qf)) & 0xFu) << (4 * e);
+          // sign-magnitude nibble: bit 3 = sign, bits 0-2 = |q| (zero stays 0)
+          const uint32_t nib = static_cast<uint32_t>(static_cast<int>(fabsf(qf))) | (qf < 0.f ? 8u : 0u);
+          word |= nib << (4 * e);
         }
         if (row_ok && g_ok)
           *reinterpret_cast<uint32_t*>(xq + xrow / 2 + (kbase + c * 32 + q * 8) / 2) = word;
@@ -194,35 +196,39 @@ __global__ __launch_bounds__(512) void k1_quant_down_int4(
 // Kernel 2: INT4 GEMM + per-group dequant + up projection + bias.
 //
 // Output tile 128 (n) x 128 (m) per workgroup of 8 waves; each wave owns a
-// 64 (n) x 32 (m) sub-tile = 4 x 2 MFMA tiles.  The MFMA computes Y^T tiles
-// (A = W codes, B = X codes) so that a lane ends up with 4 consecutive
-// output channels of one token, which it stores as one 8-byte write.  The
-// register budget is 128 VGPRs so that two workgroups (16 waves) share a CU
-// and hide memory latency.
+// 64 (n) x 32 (m) sub-tile = 2 MFMA tiles of 32 x 32.  The MFMA computes Y^T
+// tiles (A = W codes, B = X codes), so a lane ends up with groups of 4
+// consecutive output channels of one token and stores each as one 8-byte
+// write.  The register budget is 128 VGPRs: two workgroups (16 waves) share
+// a CU and hide memory latency.
 //
-// Per K-group of 64: every thread loads 16 packed bytes of one operand tile
-// from global memory two groups before they are needed (two register sets
-// used alternately), unpacks them to int8 with the x16 nibble trick
-// ((w << 4) & 0xF0F0F0F0 holds 16*q of the even codes, w & 0xF0F0F0F0 16*q
-// of the odd codes, both exact int8) and stores them into a three-slot LDS
-// ring (iteration g reads slot g%3 while g+2 is stored into slot (g+2)%3,
-// whose last readers passed the previous barrier; one barrier per group).
-// v_mfma_i32_16x16x64_i8 returns 256*P for the group, an exact int32.  The
-// dequant factor s_w[n] s_x[m] of every output element comes from a second,
-// exact matrix-core product: an f16 MFMA whose only non-zero k-slot holds
-// s_w (A) and s_x (B), so S[n][m] = s_w s_x exactly in fp32 and in the same
-// lane layout as P.  The scales sit in LDS as ready-made operands
-// (s, 0, 0, 0) so one 16-byte read fills an operand.  That leaves two VALU
-// operations per output element and group (convert, fma) instead of three:
-// on gfx950 the per-group dequant on the VALU, not the MFMA, bounds this
-// kernel.  After the K loop the 1/256 is applied, the bf16 up projection
-// runs on the same accumulators (MFMA srcC), the bias is added and Y is
-// rounded to bf16 and stored once.
+// The 4-bit codes reach the matrix core as FP8 E4M3 subnormals: a
+// sign-magnitude nibble s|mmm becomes the byte s000_0mmm, which is exactly
+// +-m * 2^-9, with four bit operations per 8 codes.  For one K-group of 64,
+// v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales) then returns P * 2^-18 in
+// fp32, exactly: every product is a multiple of 2^-18 and every partial sum
+// stays below 2^24 of those units.  So the group's integer partial P arrives
+// already as a float and the per-group dequant is one multiply (the scale
+// product s_w s_x) and one fma per output element; on gfx950 that VALU work,
+// not the MFMA, bounds the kernel.
+//
+// Per K-group: every thread loads 16 packed bytes of one operand tile from
+// global memory one group ahead (rows past the matrix edge are clamped to
+// the last row; their outputs are never stored), converts them to FP8 and
+// stores them into a three-slot LDS ring (iteration g reads slot g%3 while
+// g+2 is stored into slot (g+2)%3, whose last readers passed the previous
+// barrier; one barrier per group).  After the K loop the 2^18 is applied,
+// the bf16 up projection runs on the same accumulators (MFMA srcC), the bias
+// is added and Y is rounded to bf16 and stored once.
 // ---------------------------------------------------------------------------
 
 constexpr int kTile = 128;      // output tile edge (both n and m)
-constexpr int kLdsRow = 80;     // 64 bytes of int8 codes + 16 bytes padding
+constexpr int kLdsRow = 80;     // 64 bytes of FP8 codes + 16 bytes padding
 constexpr int kK2Threads = 512;
+constexpr unsigned kUnitScales = 0x7F7F7F7Fu;   // E8M0 127 = 1.0 in every byte
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 struct TileCoord {
   int n0, m0;
@@ -249,13 +255,16 @@ __device__ __forceinline__ TileCoord tile_coord(int pid, int tiles_n, int tiles_
   return tc;
 }
 
-__device__ __forceinline__ void unpack_store(int8_t* dst, const uint4& w) {
+// 16 packed bytes (32 sign-magnitude nibbles) -> 32 FP8 E4M3 bytes.  The
+// even codes of each packed dword go to one output dword, the odd codes to
+// the next: a fixed permutation of k that A and B share.
+__device__ __forceinline__ void unpack_store_fp8(int8_t* dst, const uint4& w) {
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
   uint32_t o[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    o[2 * i] = (ws[i] << 4) & 0xF0F0F0F0u;
-    o[2 * i + 1] = ws[i] & 0xF0F0F0F0u;
+    o[2 * i] = ((ws[i] & 0x08080808u) << 4) | (ws[i] & 0x07070707u);
+    o[2 * i + 1] = ((ws[i] >> 4) & 0x07070707u) | (ws[i] & 0x80808080u);
   }
   uint4* d = reinterpret_cast<uint4*>(dst);
   d[0] = make_uint4(o[0], o[1], o[2], o[3]);
@@ -263,7 +272,7 @@ __device__ __forceinline__ void unpack_store(int8_t* dst, const uint4& w) {
 }
 
 template <bool DEBUG>
-__global__ __launch_bounds__(kK2Threads, 4) void k2_gemm_int4(
+__global__ __launch_bounds__(kK2Threads, 4) void k2_gemm_w4a4(
     const uint8_t* __restrict__ xq, const uint16_t* __restrict__ xs,
     const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
     const float* __restrict__ lact, const uint16_t* __restrict__ lup,
@@ -277,9 +286,10 @@ __global__ __launch_bounds__(kK2Threads, 4) void k2_gemm_int4(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int r16 = lane & 15;
-  const int q = lane >> 4;
+  // wave-uniform, so that the per-wave roles below live in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
   const int wn = wave >> 2, wm = wave & 3;     // 2 x 4 waves: 64 n x 32 m each
   const int G = K / 64;
   const size_t rowb = static_cast<size_t>(K / 2);
@@ -295,21 +305,20 @@ __global__ __launch_bounds__(kK2Threads, 4) void k2_gemm_int4(
     m0 = tc.m0;
   }
 
-  // loader role: threads 0..255 move 16 packed bytes of W row t/2 (half t%2),
-  // threads 256..511 the same for X
-  const bool ld_is_w = tid < 256;
+  // loader role: threads 0..255 move 16 packed bytes of W row t/2 (half
+  // t%2), threads 256..511 the same for X; rows clamped into the matrix
+  const bool ld_is_w = wave < 4;
   const int lt = tid & 255;
   const int lrow = lt >> 1, lhalf = lt & 1;
-  const bool ld_ok = ld_is_w ? (n0 + lrow < N) : (m0 + lrow < M);
-  const uint8_t* ldsrc = (ld_is_w ? wq + static_cast<size_t>(n0 + lrow) * rowb
-                                  : xq + static_cast<size_t>(m0 + lrow) * rowb) + lhalf * 16;
+  const int src_row = ld_is_w ? min(n0 + lrow, N - 1) : min(m0 + lrow, M - 1);
+  const uint8_t* ldsrc = (ld_is_w ? wq : xq) + static_cast<size_t>(src_row) * rowb + lhalf * 16;
   int8_t* const lddst0 = (ld_is_w ? &lds_w[0][0] : &lds_x[0][0]) + lrow * kLdsRow + lhalf * 32;
   // scale role: threads 0..127 move s_w of row n0+t, 128..255 s_x of m0+t-128
-  const bool sc_thread = !DEBUG && tid < 2 * kTile;
-  const bool sc_is_w = tid < kTile;
+  const bool sc_thread = !DEBUG && wave < 4;
+  const bool sc_is_w = wave < 2;
   const int sc_i = tid & (kTile - 1);
-  const bool sc_ok = sc_thread && (sc_is_w ? (n0 + sc_i < N) : (m0 + sc_i < M));
-  const uint16_t* scsrc = DEBUG ? nullptr : (sc_is_w ? (ws + n0 + sc_i) : (xs + m0 + sc_i));
+  const int sc_row = sc_is_w ? min(n0 + sc_i, N - 1) : min(m0 + sc_i, M - 1);
+  const uint16_t* scsrc = DEBUG ? nullptr : ((sc_is_w ? ws : xs) + sc_row);
   const size_t sc_stride = sc_is_w ? static_cast<size_t>(N) : static_cast<size_t>(M);
 
   struct LoadRegs {
@@ -317,66 +326,61 @@ __global__ __launch_bounds__(kK2Threads, 4) void k2_gemm_int4(
     uint32_t sc;
   };
   auto gload = [&](int g, LoadRegs& L) {
-    L.c = ld_ok ? *reinterpret_cast<const uint4*>(ldsrc + g * 32) : make_uint4(0, 0, 0, 0);
-    if constexpr (!DEBUG) L.sc = sc_ok ? static_cast<uint32_t>(scsrc[static_cast<size_t>(g) * sc_stride]) : 0u;
+    L.c = *reinterpret_cast<const uint4*>(ldsrc + g * 32);
+    if constexpr (!DEBUG) {
+      if (sc_thread) L.sc = scsrc[static_cast<size_t>(g) * sc_stride];
+    }
   };
   auto lstore = [&](int g, const LoadRegs& L) {
     const int buf = g % 3;
-    unpack_store(lddst0 + buf * (kTile * kLdsRow), L.c);
+    unpack_store_fp8(lddst0 + buf * (kTile * kLdsRow), L.c);
     if constexpr (!DEBUG) {
       if (sc_thread) {
-        // s_x carries the 1/256 of the x16 nibble trick (exact)
-        const float v = f16_bits_to_f32(L.sc) * (sc_is_w ? 1.0f : 0.00390625f);
         float* dst = sc_is_w ? &lds_sw[buf][sc_i] : &lds_sx[buf][sc_i];
-        *dst = v;
+        *dst = f16_bits_to_f32(L.sc);
       }
     }
   };
 
-  v4f acc[4][2];
+  v16f acc[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int it = 0; it < 2; ++it)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < 16; ++r) acc[it][r] = 0.f;
 
   auto compute = [&](int g) {
     const int buf = g % 3;
-    v4i a[4], b[2];
+    const int8_t* xrow = &lds_x[buf][(wm * 32 + l32) * kLdsRow + 32 * h];
+    const v8i b = __builtin_shufflevector(*reinterpret_cast<const v4i*>(xrow),
+                                          *reinterpret_cast<const v4i*>(xrow + 16), 0, 1, 2, 3, 4, 5, 6, 7);
+    float sx = 0.f;
+    if constexpr (!DEBUG) sx = lds_sx[buf][wm * 32 + l32];
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
-      a[it] = *reinterpret_cast<const v4i*>(&lds_w[buf][(wn * 64 + it * 16 + r16) * kLdsRow + q * 16]);
+    for (int it = 0; it < 2; ++it) {
+      const int8_t* wrow = &lds_w[buf][(wn * 64 + it * 32 + l32) * kLdsRow + 32 * h];
+      const v8i a = __builtin_shufflevector(*reinterpret_cast<const v4i*>(wrow),
+                                            *reinterpret_cast<const v4i*>(wrow + 16), 0, 1, 2, 3, 4, 5, 6, 7);
+      const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, v16f{}, 0, 0, 0, kUnitScales, 0,
+                                                                     kUnitScales);
+      if constexpr (DEBUG) {
+        const int m = m0 + wm * 32 + l32;
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-      b[jt] = *reinterpret_cast<const v4i*>(&lds_x[buf][(wm * 32 + jt * 16 + r16) * kLdsRow + q * 16]);
-    v4f sw4[4];
-    float sx1[2];
-    if constexpr (!DEBUG) {
+        for (int r = 0; r < 16; ++r) {
+          const int n = n0 + wn * 64 + it * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+          if (m < win_m0 + win_mt && n < win_n0 + win_nt)
+            dbg[(static_cast<size_t>(m - win_m0) * win_nt + (n - win_n0)) * G + g] =
+                static_cast<int32_t>(p[r] * 262144.0f);     // exact: P * 2^-18 * 2^18
+        }
+      } else {
 #pragma unroll
-      for (int it = 0; it < 4; ++it) sw4[it] = *reinterpret_cast<const v4f*>(&lds_sw[buf][wn * 64 + it * 16 + 4 * q]);
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) sx1[jt] = lds_sx[buf][wm * 32 + jt * 16 + r16];
-    }
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        const v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[it], b[jt], v4i{0, 0, 0, 0}, 0, 0, 0);
-        if constexpr (DEBUG) {
-          const int m = m0 + wm * 32 + jt * 16 + r16;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int n = n0 + wn * 64 + it * 16 + 4 * q + i;
-            if (m < win_m0 + win_mt && n < win_n0 + win_nt) {
-              dbg[(static_cast<size_t>(m - win_m0) * win_nt + (n - win_n0)) * G + g] = p[i] >> 8;
-            }
-          }
-        } else {
+        for (int j = 0; j < 4; ++j) {
+          const v4f sw4 = *reinterpret_cast<const v4f*>(&lds_sw[buf][wn * 64 + it * 32 + 8 * j + 4 * h]);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            acc[it][jt][i] = __builtin_fmaf(static_cast<float>(p[i]), sw4[it][i] * sx1[jt], acc[it][jt][i]);
+            acc[it][4 * j + i] = __builtin_fmaf(p[4 * j + i], sw4[i] * sx, acc[it][4 * j + i]);
         }
       }
-      // one row tile's products in flight at a time (register budget)
+      // one tile's products in flight at a time (register budget)
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -404,63 +408,57 @@ __global__ __launch_bounds__(kK2Threads, 4) void k2_gemm_int4(
   }
 
   if constexpr (!DEBUG) {
-    // up projection: acc += bf16(lora_act) . L2 on the same tiles
-    for (int c0 = 0; c0 < rank; c0 += 32) {
-      const int j = c0 + 8 * q;          // this lane's 8 k-slots
-      const bool j_ok = j < rank;
-      v4i ua[4], ub[2];
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int n = n0 + wn * 64 + it * 16 + r16;
-        ua[it] = (j_ok && n < N) ? *reinterpret_cast<const v4i*>(lup + static_cast<size_t>(n) * rank + j)
-                                 : v4i{0, 0, 0, 0};
+    for (int it = 0; it < 2; ++it) acc[it] *= 262144.0f;   // 2^18, exact
+
+    // up projection: acc += bf16(lora_act) . L2 on the same tiles, K = 16
+    // per v_mfma_f32_32x32x16_bf16 (rank is a multiple of 16)
+    const int m = m0 + wm * 32 + l32;
+    for (int c0 = 0; c0 < rank; c0 += 16) {
+      const int j = c0 + 8 * h;          // this lane's 8 k-slots
+      v4i ub = v4i{0, 0, 0, 0};
+      if (m < M) {
+        const float4* src = reinterpret_cast<const float4*>(lact + static_cast<size_t>(m) * rank + j);
+        const float4 f0 = src[0], f1 = src[1];
+        ub = v4i{static_cast<int>(pack_bf16_rne(f0.x, f0.y)), static_cast<int>(pack_bf16_rne(f0.z, f0.w)),
+                 static_cast<int>(pack_bf16_rne(f1.x, f1.y)), static_cast<int>(pack_bf16_rne(f1.z, f1.w))};
       }
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        const int m = m0 + wm * 32 + jt * 16 + r16;
-        if (j_ok && m < M) {
-          const float4* src = reinterpret_cast<const float4*>(lact + static_cast<size_t>(m) * rank + j);
-          const float4 f0 = src[0], f1 = src[1];
-          ub[jt] = v4i{static_cast<int>(pack_bf16_rne(f0.x, f0.y)), static_cast<int>(pack_bf16_rne(f0.z, f0.w)),
-                       static_cast<int>(pack_bf16_rne(f1.x, f1.y)), static_cast<int>(pack_bf16_rne(f1.z, f1.w))};
-        } else {
-          ub[jt] = v4i{0, 0, 0, 0};
-        }
+      for (int it = 0; it < 2; ++it) {
+        const int n = n0 + wn * 64 + it * 32 + l32;
+        const v4i ua = n < N ? *reinterpret_cast<const v4i*>(lup + static_cast<size_t>(n) * rank + j)
+                             : v4i{0, 0, 0, 0};
+        acc[it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ua), __builtin_bit_cast(v8bf, ub),
+                                                         acc[it], 0, 0, 0);
       }
-#pragma unroll
-      for (int it = 0; it < 4; ++it)
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
-          acc[it][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, ua[it]),
-                                                               __builtin_bit_cast(v8bf, ub[jt]), acc[it][jt], 0, 0, 0);
     }
 
-    const bool vec_ok = (N % 4) == 0;
+    if (m < M) {
+      const bool vec_ok = (N % 4) == 0;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int nb = n0 + wn * 64 + it * 16 + 4 * q;
-      float bv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (bias) {
+      for (int it = 0; it < 2; ++it) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (nb + i < N) bv[i] = __uint_as_float(static_cast<uint32_t>(bias[nb + i]) << 16);
-      }
+        for (int j = 0; j < 4; ++j) {
+          const int nb = n0 + wn * 64 + it * 32 + 8 * j + 4 * h;    // 4 consecutive channels
+          float bv[4] = {0.f, 0.f, 0.f, 0.f};
+          if (bias) {
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        const int m = m0 + wm * 32 + jt * 16 + r16;
-        if (m >= M) continue;
-        uint16_t* dst = y + static_cast<size_t>(m) * N + nb;
-        const uint32_t h0 = bf16_rne_bits(acc[it][jt][0] + bv[0]);
-        const uint32_t h1 = bf16_rne_bits(acc[it][jt][1] + bv[1]);
-        const uint32_t h2 = bf16_rne_bits(acc[it][jt][2] + bv[2]);
-        const uint32_t h3 = bf16_rne_bits(acc[it][jt][3] + bv[3]);
-        if (vec_ok && nb + 3 < N) {
-          *reinterpret_cast<uint2*>(dst) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-        } else {
-          const uint32_t hs[4] = {h0, h1, h2, h3};
+            for (int i = 0; i < 4; ++i)
+              if (nb + i < N) bv[i] = __uint_as_float(static_cast<uint32_t>(bias[nb + i]) << 16);
+          }
+          uint16_t* dst = y + static_cast<size_t>(m) * N + nb;
+          const uint32_t h0 = bf16_rne_bits(acc[it][4 * j + 0] + bv[0]);
+          const uint32_t h1 = bf16_rne_bits(acc[it][4 * j + 1] + bv[1]);
+          const uint32_t h2 = bf16_rne_bits(acc[it][4 * j + 2] + bv[2]);
+          const uint32_t h3 = bf16_rne_bits(acc[it][4 * j + 3] + bv[3]);
+          if (vec_ok && nb + 3 < N) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+          } else {
+            const uint32_t hs[4] = {h0, h1, h2, h3};
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (nb + i < N) dst[i] = static_cast<uint16_t>(hs[i]);
+            for (int i = 0; i < 4; ++i)
+              if (nb + i < N) dst[i] = static_cast<uint16_t>(hs[i]);
+          }
         }
       }
     }
@@ -473,7 +471,7 @@ hipError_t launch_k1(const void* x, int M, int K, const float* sinv, const void*
   const int G = K / 64;
   const int nsteps = (G + 1) / 2;
   int waves = nsteps < 8 ? nsteps : 8;
-  if (RT > 0) {
+  if constexpr (RT > 0) {
     const int lds_cap = 1024 / (RT * 16);     // W * 16 * RANK * 4 bytes <= 64 KiB
     if (waves > lds_cap) waves = lds_cap;
   }
@@ -513,7 +511,7 @@ extern "C" int svdq_launch_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs, 
                                              int M, int N, int K, int rank, int precision, void* stream) {
   if (precision != SVDQ_INT4) return static_cast<int>(hipErrorInvalidValue);
   const int tiles = ((N + kTile - 1) / kTile) * ((M + kTile - 1) / kTile);
-  hipLaunchKernelGGL(k2_gemm_int4<false>, dim3(tiles), dim3(kK2Threads), 0, static_cast<hipStream_t>(stream), xq,
+  hipLaunchKernelGGL(k2_gemm_w4a4<false>, dim3(tiles), dim3(kK2Threads), 0, static_cast<hipStream_t>(stream), xq,
                      static_cast<const uint16_t*>(xs), wq, static_cast<const uint16_t*>(ws), lora_act,
                      static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias),
                      static_cast<uint16_t*>(y), M, N, K, rank, 0, 0, 0, 0, nullptr);
@@ -523,7 +521,7 @@ extern "C" int svdq_launch_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs, 
 extern "C" int svdq_launch_debug_group_partials(const uint8_t* xq, const uint8_t* wq, int M, int N, int K, int m0,
                                                 int n0, int mt, int nt, int32_t* out, void* stream) {
   const int tiles = ((nt + kTile - 1) / kTile) * ((mt + kTile - 1) / kTile);
-  hipLaunchKernelGGL(k2_gemm_int4<true>, dim3(tiles), dim3(kK2Threads), 0, static_cast<hipStream_t>(stream), xq, nullptr,
+  hipLaunchKernelGGL(k2_gemm_w4a4<true>, dim3(tiles), dim3(kK2Threads), 0, static_cast<hipStream_t>(stream), xq, nullptr,
                      wq, nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, 0, m0, n0, mt, nt, out);
   return static_cast<int>(hipGetLastError());
 }

@@ -379,7 +379,10 @@ void quant_int4_row(const float* v, int K, uint8_t* q_packed, uint16_t* scale_bi
       int q1 = static_cast<int>(std::nearbyint(gv[i + 1] * inv));
       q0 = std::min(7, std::max(-7, q0));
       q1 = std::min(7, std::max(-7, q1));
-      out[i / 2] = static_cast<uint8_t>((q0 & 0xF) | ((q1 & 0xF) << 4));
+      // sign-magnitude nibbles: bit 3 = sign, bits 0-2 = |q|
+      const int n0 = q0 < 0 ? (8 | -q0) : q0;
+      const int n1 = q1 < 0 ? (8 | -q1) : q1;
+      out[i / 2] = static_cast<uint8_t>(n0 | (n1 << 4));
     }
   }
 }

@@ -32,8 +32,9 @@
  *    stored the same way: lora_down = L1^T as [rank][K] and lora_up = L2^T
  *    as [N][rank], i.e. the weights of the two small linears K->rank and
  *    rank->N.
- *  - INT4 codes: two's-complement nibbles in [-7, 7], code k in the low
- *    nibble of byte k/2 when k is even; rows of K/2 bytes.
+ *  - INT4 codes: sign-magnitude nibbles (bit 3 = sign, bits 0-2 = |q|,
+ *    q in [-7, 7], zero stored as 0), code k in the low nibble of byte k/2
+ *    when k is even; rows of K/2 bytes.
  *    INT4 scales: fp16, one per 64 consecutive k of a row, group-major
  *    [K/64][rows].  MXFP4 codes: E2M1 nibbles (sign in bit 3), same packing;
  *    MXFP4 scales: E8M0 bytes, one per 32 k, group-major [K/32][rows].
