@@ -12,7 +12,15 @@ in HBM; four copies of every buffer are rotated so that the 256 MB
 Infinity Cache cannot hold a step's working set.
 
 Prints one JSON line.  `value` is the whole step's effective throughput
-(2*M*N*K summed over both layers / step time) in TOPS.
+(2*M*N*K summed over both layers / step time) in TOPS.  `roofline` is that
+of the dominant kernel, the 4-bit GEMM + up projection: its algorithmic
+ops (2*M*N*K, the same for fc1 and fc2) over its average launch time,
+timed with HIP events on the stream the library launches on, against the
+dense 8-bit matrix-core peak (int8 and fp8 run at the same rate).
+
+`--calibrate-copy` instead runs a plain elementwise copy of 1 GiB a few
+times; its FETCH_SIZE / WRITE_SIZE counters give the factor that turns the
+counters read on the GEMM into HBM bytes.
 """
 
 from __future__ import annotations
@@ -28,10 +36,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = ("fused W4A4+LoRA-r32 linear: µs/layer, TOPS & % INT8-MFMA roofline (FLUX MLP)")
-INT8_PEAK_TOPS = 5033.0        # 256 CU x 2.4 GHz x 8192 int8 ops/clk/CU (dense)
+INT8_PEAK_TOPS = 5033.0        # 256 CU x 2.4 GHz x 8192 int8/fp8 ops/clk/CU (dense)
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "bit_quantized_diffusion_amd", "csrc", "svdq_kernels.hip")
-COUNTERS = os.path.join(ROOT, "profiles", "k2_gemm_fc1_counters.json")
+TRAFFIC = os.path.join(ROOT, "profiles", "k2_gemm_w4a4_flux_mlp_hbm_traffic.md")
+TRAFFIC_NOTE = ("rocprofv3 FETCH_SIZE + WRITE_SIZE per launch, scaled by the elementwise-copy "
+                "calibration (profiles/k2_gemm_w4a4_flux_mlp_hbm_traffic.md)")
 
 
 def log(*a):
@@ -50,12 +60,47 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--sets", type=int, default=4, help="rotated buffer sets")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=96, help="token rows in the oracle sample")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="time budget of the oracle sample (whole chunks of rows)")
+    p.add_argument("--cpu-chunk", type=int, default=96, help="token rows per oracle chunk")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run a 1 GiB elementwise copy (counter calibration) and exit")
     return p.parse_args()
+
+
+def calibrate_copy():
+    """A plain copy of known size: 2^28 fp32 read and 2^28 fp32 written per
+    launch (torch.neg into a second buffer, one elementwise kernel)."""
+    import torch
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "elementwise copy", "bytes_read_per_launch": 4 * n,
+                      "bytes_written_per_launch": 4 * n, "launches": 5}), flush=True)
+
+
+def read_traffic():
+    """HBM bytes per GEMM launch from the committed counter summary, if it
+    was taken on the current kernel source."""
+    import re
+    if not os.path.exists(TRAFFIC):
+        return None, None
+    text = open(TRAFFIC).read()
+    sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not sha or not val or sha.group(1) != kernel_sha():
+        return None, "stale" if sha else None
+    return float(val.group(1)), "fresh"
 
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported "
                           "(token rows shard across GPUs with no exchange; see the design notes)"}))
@@ -168,27 +213,29 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     value = ops_total / (ms_per_step * 1e-3) / 1e12
 
-    # roofline of the dominant kernel: the fc1 4-bit GEMM
-    k2_us = per["fc1"]["us_k2"]
-    achieved = 2.0 * s1.M * s1.N * s1.K / (k2_us * 1e-6) / 1e12
-    traffic = None
-    if os.path.exists(COUNTERS):
-        with open(COUNTERS) as fh:
-            c = json.load(fh)
-        if c.get("kernel_sha") == kernel_sha():
-            traffic = c.get("hbm_bytes_per_launch")
+    # roofline of the dominant kernel: the 4-bit GEMM + up projection, over
+    # all its launches (fc1 and fc2 carry the same 2*M*N*K)
+    k2_us = float(np.mean([x[1].elapsed_time(x[2]) for t in ("fc1", "fc2") for x in ev[t]])) * 1e3
+    k2_ops = 2.0 * s1.M * s1.N * s1.K
+    assert k2_ops == 2.0 * s2.M * s2.N * s2.K
+    achieved = k2_ops / (k2_us * 1e-6) / 1e12
+    traffic, traffic_state = read_traffic()
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic,
-                "kernel": "k2_gemm_int4 (fc1 4608x3072x12288)", "ops": "int8 MFMA ops"}
+                "kernel": "k2_gemm_w4a4 (fc1 4608x3072->12288 and fc2 4608x12288->3072)",
+                "avg_launch_us": round(k2_us, 2), "ops_per_launch": k2_ops,
+                "peak_basis": "dense int8/fp8 matrix-core rate, 256 CU x 2.4 GHz x 8192 ops/clk",
+                "traffic_source": TRAFFIC_NOTE if traffic is not None else
+                ("counter summary taken on older kernel source" if traffic_state == "stale" else None)}
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(lay1, pk1, s1, args.cpu_rows)
+        cpu = cpu_baseline(lay1, pk1, s1, args.cpu_seconds, args.cpu_chunk)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int4",
         "data": "synthetic",
         "config": {"workload": "FLUX.1 MLP pair at 1024x1024: fc1 4608x3072->12288 + fc2 4608x12288->3072, "
                                "rank 32, int4 g64 W4A4, bf16 in/out, bias",
@@ -200,9 +247,10 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(lay1, pk1, spec, rows):
-    """The oracle's online path (both fused kernels' steps) for `rows` token
-    rows of fc1 on the host cores, scaled to TOPS."""
+def cpu_baseline(lay1, pk1, spec, seconds, chunk):
+    """The oracle's online path (both fused kernels' steps) on whole chunks
+    of fc1 token rows, spread over the token range, until `seconds` of host
+    time are spent; scaled to TOPS."""
     import numpy as np
     import oracle as O
     try:
@@ -210,19 +258,25 @@ def cpu_baseline(lay1, pk1, spec, rows):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
     except Exception:
         threads = os.cpu_count()
-    sel = np.linspace(0, spec.M - 1, rows).astype(np.int64)
-    x = np.ascontiguousarray(lay1["x"][sel])
     l1 = np.ascontiguousarray(pk1["lora_down"].T)
     l2 = np.ascontiguousarray(pk1["lora_up"].T)
+    n_chunks = spec.M // chunk
+    order = np.random.default_rng(0).permutation(n_chunks)
+    rows = 0
     t0 = time.perf_counter()
-    a = O.quantize_act_lora_down(x, pk1["smooth_inv"], l1)
-    O.gemm_w4a4_lora_up(a["xq"], a["xs"], pk1["wq"], pk1["ws"], a["t"], l2, lay1["bias"])
+    for c in order:
+        x = np.ascontiguousarray(lay1["x"][c * chunk:(c + 1) * chunk])
+        a = O.quantize_act_lora_down(x, pk1["smooth_inv"], l1)
+        O.gemm_w4a4_lora_up(a["xq"], a["xs"], pk1["wq"], pk1["ws"], a["t"], l2, lay1["bias"])
+        rows += chunk
+        if time.perf_counter() - t0 >= seconds:
+            break
     dt = time.perf_counter() - t0
     ops = 2.0 * rows * spec.N * spec.K
     log(f"bench: cpu oracle {rows} rows of fc1 in {dt:.1f} s")
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": int(threads), "kind": "oracle",
-            "sample": f"{rows} of {spec.M} token rows of fc1 ({spec.K}->{spec.N}, rank {spec.rank}), "
-                      f"quantize+down and per-group GEMM+up, {dt:.1f} s",
+            "sample": f"{rows} of {spec.M} token rows of fc1 ({spec.K}->{spec.N}, rank {spec.rank}) in "
+                      f"chunks of {chunk}: quantize+down and per-group GEMM+up, {dt:.1f} s",
             "us_per_layer_equiv": round(dt / rows * spec.M * 1e6, 1)}
 
 
