@@ -68,24 +68,33 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
 //
 // A workgroup owns 16 rows and all of K, with W waves (W = blockDim/64).  A
 // wave step covers the 16 rows x 2 groups (128 k): lane l owns row l % 16
-// and, for chunk c = 0..3 of 32 k, the 8 k at c*32 + (l/16)*8, so every
-// load instruction reads 64 contiguous bytes of each of 16 rows.  The group
-// absmax is combined over the 4 lanes of a row with two lane exchanges.  X^
-// is rounded to bf16 by v_cvt_pk_bf16_f32; the packed pairs are the A
-// operand of the bf16 MFMA with L1 (K = 32 per chunk), so X is read once.
-// Waves take steps round-robin and their partial X^ L1 tiles are summed in
-// LDS in a fixed order (deterministic).
+// and the 32 contiguous k at (l/16)*32, half of one group, read as 4 chunks
+// of 8 k.  The group absmax needs one lane exchange (the other half is 16
+// lanes away), and the lane's 32 codes leave as one 16-byte store.  X^ is
+// rounded to bf16 by v_cvt_pk_bf16_f32; chunk c of the 4 lanes of a row is
+// the A operand of one bf16 MFMA with L1 (K = 32: k at q*32 + c*8 + 0..7 for
+// lane group q; the L1 fragment is loaded with the same k), so X is read
+// once.  Waves take steps round-robin and their partial X^ L1 tiles are
+// summed in LDS in a fixed order (deterministic).
+//
+// The kernel is bound by HBM reads of X, so every load is unconditional
+// (row and k clamped into the matrix; data of a clamped chunk is zeroed
+// before use, stores are predicated) and the X of a wave's next step is
+// requested before the current step is processed: a wave keeps a step of X
+// and the current step's L1 fragments in flight instead of one round trip
+// per load.
 // ---------------------------------------------------------------------------
 
-template <int RT>
-__global__ __launch_bounds__(512) void k1_quant_down_int4(
+template <int RT, bool SINV_LDS>
+__global__ __launch_bounds__(512, RT <= 2 ? 4 : 2) void k1_quant_down_int4(
     const uint16_t* __restrict__ x, int M, int K, const float* __restrict__ sinv,
     const uint16_t* __restrict__ ldown, uint8_t* __restrict__ xq, uint16_t* __restrict__ xs,
     float* __restrict__ lact) {
   constexpr int RANK = RT * 16;
-  extern __shared__ float red[];            // [W][16][RANK]
+  constexpr int TB = RT < 2 ? (RT > 0 ? RT : 1) : 2;    // L1 fragments per batch of loads (ranks of 16)
+  extern __shared__ float red[];            // [W][16][RANK], then smooth_inv [K] when SINV_LDS
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int W = blockDim.x >> 6;
   const int r16 = lane & 15;
   const int q = lane >> 4;
@@ -95,83 +104,128 @@ __global__ __launch_bounds__(512) void k1_quant_down_int4(
   const int G = K / 64;
   const int nsteps = (G + 1) / 2;
   const size_t xrow = static_cast<size_t>(row) * K;
+  const uint16_t* xr = x + static_cast<size_t>(min(row, M - 1)) * K;
+  // k of chunk c of a step for this lane, clamped into the row
+  auto kof = [&](int step, int c) { return min(step * 128 + q * 32 + c * 8, K - 8); };
 
   v4f acc[RT > 0 ? RT : 1];
 #pragma unroll
   for (int t = 0; t < (RT > 0 ? RT : 1); ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // smooth_inv is read by every step of every wave: stage it in LDS once per
+  // workgroup so that its reads cost an LDS round trip, not an L2 one
+  float* const lds_sinv = red + (RT > 0 ? W * 16 * RANK : 0);
+  if constexpr (SINV_LDS) {
+    for (int i = threadIdx.x; i < K / 4; i += blockDim.x)
+      reinterpret_cast<float4*>(lds_sinv)[i] = reinterpret_cast<const float4*>(sinv)[i];
+    __syncthreads();
+  }
+  const float* const sv = SINV_LDS ? lds_sinv : sinv;
+
+  uint4 xn[4];
+  {
+    const int first = min(wave, nsteps - 1);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) xn[c] = *reinterpret_cast<const uint4*>(xr + kof(first, c));
+  }
+
   for (int step = wave; step < nsteps; step += W) {
     const int kbase = step * 128;
+    uint4 xc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) xc[c] = xn[c];
+    {
+      const int nxt = min(step + W, nsteps - 1);        // the last step re-reads itself (unused)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xn[c] = *reinterpret_cast<const uint4*>(xr + kof(nxt, c));
+    }
+    float4 s0[4], s1[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      s0[c] = *reinterpret_cast<const float4*>(sv + kof(step, c));
+      s1[c] = *reinterpret_cast<const float4*>(sv + kof(step, c) + 4);
+    }
+    // first batch of L1 fragments, in flight during the quantization
+    v4i lb[4][TB];
+    if constexpr (RT > 0) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+          lb[c][t] = *reinterpret_cast<const v4i*>(ldown + static_cast<size_t>(t * 16 + r16) * K + kof(step, c));
+    }
+
+    // lane (row, q) holds the 32 k at kbase + q*32: half of group
+    // step*2 + q/2, whose other half sits in lane q^1 (16 lanes away)
+    const bool valid = kbase + q * 32 < K;             // false only in the odd last group
     float xh[4][8];
     uint32_t pk[4][4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int kc = kbase + c * 32 + q * 8;
-      const bool valid = kbase + c * 32 < K;
-      uint4 w = make_uint4(0, 0, 0, 0);
-      float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
-      if (valid) {
-        if (row_ok) w = *reinterpret_cast<const uint4*>(x + xrow + kc);
-        s0 = *reinterpret_cast<const float4*>(sinv + kc);
-        s1 = *reinterpret_cast<const float4*>(sinv + kc + 4);
-      }
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-      const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      const uint32_t ws[4] = {xc[c].x, xc[c].y, xc[c].z, xc[c].w};
+      const float ss[8] = {s0[c].x, s0[c].y, s0[c].z, s0[c].w, s1[c].x, s1[c].y, s1[c].z, s1[c].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float lo = __uint_as_float(ws[e] << 16) * ss[2 * e];
         const float hi = __uint_as_float(ws[e] & 0xFFFF0000u) * ss[2 * e + 1];
-        const uint32_t p = cvt_pk_bf16(lo, hi);
+        const uint32_t p = valid ? cvt_pk_bf16(lo, hi) : 0u;
         pk[c][e] = p;
         xh[c][2 * e] = __uint_as_float(p << 16);
         xh[c][2 * e + 1] = __uint_as_float(p & 0xFFFF0000u);
       }
     }
 
-    // two groups per step: chunks {0,1} and {2,3}
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int g = step * 2 + j;
+    {
+      const int g = step * 2 + (q >> 1);
       float amax = 0.f;
 #pragma unroll
-      for (int c = 2 * j; c < 2 * j + 2; ++c)
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(xh[c][e]));
       amax = fmaxf(amax, __shfl_xor(amax, 16));
-      amax = fmaxf(amax, __shfl_xor(amax, 32));
       const uint32_t sbits = f16_sat_bits(__fdiv_rn(amax, 7.0f));
       const float s = f16_bits_to_f32(sbits);
       const float inv = (s == 0.f) ? 0.f : __fdiv_rn(1.0f, s);
-      const bool g_ok = g < G;
+      uint32_t word[4];
 #pragma unroll
-      for (int c = 2 * j; c < 2 * j + 2; ++c) {
-        uint32_t word = 0;
+      for (int c = 0; c < 4; ++c) {
+        word[c] = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float qf = __builtin_rintf(xh[c][e] * inv);
           qf = fminf(7.f, fmaxf(-7.f, qf));
           // sign-magnitude nibble: bit 3 = sign, bits 0-2 = |q| (zero stays 0)
           const uint32_t nib = static_cast<uint32_t>(static_cast<int>(fabsf(qf))) | (qf < 0.f ? 8u : 0u);
-          word |= nib << (4 * e);
+          word[c] |= nib << (4 * e);
         }
-        if (row_ok && g_ok)
-          *reinterpret_cast<uint32_t*>(xq + xrow / 2 + (kbase + c * 32 + q * 8) / 2) = word;
       }
-      if (row_ok && g_ok && q == j) xs[static_cast<size_t>(g) * M + row] = static_cast<uint16_t>(sbits);
+      // the lane's 32 codes are 16 contiguous bytes of the packed row
+      if (row_ok && valid)
+        *reinterpret_cast<uint4*>(xq + xrow / 2 + (kbase + q * 32) / 2) = make_uint4(word[0], word[1], word[2], word[3]);
+      if (row_ok && valid && (q & 1) == 0) xs[static_cast<size_t>(g) * M + row] = static_cast<uint16_t>(sbits);
     }
 
     if constexpr (RT > 0) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int kc = kbase + c * 32 + q * 8;
-        const bool valid = kbase + c * 32 < K;
-        const v8bf a = __builtin_bit_cast(v8bf, (v4i{static_cast<int>(pk[c][0]), static_cast<int>(pk[c][1]),
-                                                     static_cast<int>(pk[c][2]), static_cast<int>(pk[c][3])}));
+      for (int t0 = 0; t0 < RT; t0 += TB) {
+        if (t0 > 0) {
 #pragma unroll
-        for (int t = 0; t < RT; ++t) {
-          v4i braw = v4i{0, 0, 0, 0};
-          if (valid) braw = *reinterpret_cast<const v4i*>(ldown + static_cast<size_t>(t * 16 + r16) * K + kc);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, braw), acc[t], 0, 0, 0);
+          for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
+              if (t0 + t < RT)
+                lb[c][t] = *reinterpret_cast<const v4i*>(ldown + static_cast<size_t>((t0 + t) * 16 + r16) * K +
+                                                         kof(step, c));
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const v8bf a = __builtin_bit_cast(v8bf, (v4i{static_cast<int>(pk[c][0]), static_cast<int>(pk[c][1]),
+                                                       static_cast<int>(pk[c][2]), static_cast<int>(pk[c][3])}));
+#pragma unroll
+          for (int t = 0; t < TB; ++t)
+            if (t0 + t < RT)    // compile-time after unrolling (odd RT)
+              acc[t0 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, lb[c][t]),
+                                                                    acc[t0 + t], 0, 0, 0);
         }
       }
     }
@@ -229,6 +283,11 @@ constexpr unsigned kUnitScales = 0x7F7F7F7Fu;   // E8M0 127 = 1.0 in every byte
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+template <int S>
+struct Slot {
+  static constexpr int value = S;
+};
 
 struct TileCoord {
   int n0, m0;
@@ -281,8 +340,10 @@ __global__ __launch_bounds__(kK2Threads, 4) void k2_gemm_w4a4(
     int win_m0, int win_n0, int win_mt, int win_nt, int32_t* __restrict__ dbg) {
   __shared__ __attribute__((aligned(16))) int8_t lds_w[3][kTile * kLdsRow];
   __shared__ __attribute__((aligned(16))) int8_t lds_x[3][kTile * kLdsRow];
-  __shared__ __attribute__((aligned(16))) float lds_sw[DEBUG ? 1 : 3][kTile];
-  __shared__ float lds_sx[DEBUG ? 1 : 3][kTile];
+  // per group and row: E8M0 exponent byte of the scale (as a dword) and
+  // the fp16 significand in [1, 2); index 0 = W rows, 1 = X rows
+  __shared__ __attribute__((aligned(16))) uint32_t lds_se[DEBUG ? 1 : 3][2][kTile];
+  __shared__ __attribute__((aligned(16))) _Float16 lds_sm[DEBUG ? 1 : 3][2][kTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -331,13 +392,23 @@ __global__ __launch_bounds__(kK2Threads, 4) void k2_gemm_w4a4(
       if (sc_thread) L.sc = scsrc[static_cast<size_t>(g) * sc_stride];
     }
   };
-  auto lstore = [&](int g, const LoadRegs& L) {
-    const int buf = g % 3;
+  // store one group into ring slot BUF.  A scale s (fp16, >= 0) is split
+  // into its binary exponent, which the matrix core applies exactly as an
+  // E8M0 block scale, and its significand in [1, 2), an exact fp16.  Taken
+  // from the fp32 image of s (normal for every fp16 value): the exponent
+  // byte is the fp32 exponent field.  W rows carry an extra 2^18 that
+  // cancels the 2^-18 of the FP8 code encoding.  s == 0 gives byte 0
+  // (2^-127) with significand 1; its codes are all 0, so its products are 0.
+  auto lstore = [&](auto buf_c, const LoadRegs& L) {
+    constexpr int buf = decltype(buf_c)::value;
     unpack_store_fp8(lddst0 + buf * (kTile * kLdsRow), L.c);
     if constexpr (!DEBUG) {
       if (sc_thread) {
-        float* dst = sc_is_w ? &lds_sw[buf][sc_i] : &lds_sx[buf][sc_i];
-        *dst = f16_bits_to_f32(L.sc);
+        const uint32_t u = __float_as_uint(f16_bits_to_f32(L.sc));
+        const uint32_t ebyte = ((u >> 23) & 0xFFu) + (sc_is_w && u != 0 ? 18u : 0u);
+        lds_se[buf][sc_is_w ? 0 : 1][sc_i] = ebyte;
+        lds_sm[buf][sc_is_w ? 0 : 1][sc_i] =
+            static_cast<_Float16>(__uint_as_float((u & 0x007FFFFFu) | 0x3F800000u));
       }
     }
   };
@@ -348,21 +419,31 @@ __global__ __launch_bounds__(kK2Threads, 4) void k2_gemm_w4a4(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[it][r] = 0.f;
 
-  auto compute = [&](int g) {
-    const int buf = g % 3;
+  // Per group and 32x32 tile the MFMA returns P * 2^(e_w + e_x) (exact:
+  // the E8M0 scales are powers of two and every value stays a normal fp32);
+  // the significands multiply in packed fp16 (m_w m_x in [1, 4), one
+  // rounding, relative error <= 2^-11) and v_fma_mix_f32 adds P' * (m_w m_x)
+  // into the fp32 accumulator: 1.5 VALU operations per output and group.
+  auto compute = [&](int g, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
     const int8_t* xrow = &lds_x[buf][(wm * 32 + l32) * kLdsRow + 32 * h];
     const v8i b = __builtin_shufflevector(*reinterpret_cast<const v4i*>(xrow),
                                           *reinterpret_cast<const v4i*>(xrow + 16), 0, 1, 2, 3, 4, 5, 6, 7);
-    float sx = 0.f;
-    if constexpr (!DEBUG) sx = lds_sx[buf][wm * 32 + l32];
+    uint32_t eb = 127u;
+    h2 mx2 = h2{static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+    if constexpr (!DEBUG) {
+      eb = lds_se[buf][1][wm * 32 + l32];
+      const _Float16 mx = lds_sm[buf][1][wm * 32 + l32];
+      mx2 = h2{mx, mx};
+    }
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int8_t* wrow = &lds_w[buf][(wn * 64 + it * 32 + l32) * kLdsRow + 32 * h];
       const v8i a = __builtin_shufflevector(*reinterpret_cast<const v4i*>(wrow),
                                             *reinterpret_cast<const v4i*>(wrow + 16), 0, 1, 2, 3, 4, 5, 6, 7);
-      const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, v16f{}, 0, 0, 0, kUnitScales, 0,
-                                                                     kUnitScales);
       if constexpr (DEBUG) {
+        const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, v16f{}, 0, 0, 0, kUnitScales, 0,
+                                                                       kUnitScales);
         const int m = m0 + wm * 32 + l32;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -372,12 +453,18 @@ __global__ __launch_bounds__(kK2Threads, 4) void k2_gemm_w4a4(
                 static_cast<int32_t>(p[r] * 262144.0f);     // exact: P * 2^-18 * 2^18
         }
       } else {
+        const uint32_t ea = lds_se[buf][0][wn * 64 + it * 32 + l32];
+        const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, v16f{}, 0, 0, 0, ea, 0, eb);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const v4f sw4 = *reinterpret_cast<const v4f*>(&lds_sw[buf][wn * 64 + it * 32 + 8 * j + 4 * h]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[it][4 * j + i] = __builtin_fmaf(p[4 * j + i], sw4[i] * sx, acc[it][4 * j + i]);
+          // significands of the 4 consecutive W rows this lane's elements 4j..4j+3 belong to
+          const uint2 mw = *reinterpret_cast<const uint2*>(&lds_sm[buf][0][wn * 64 + it * 32 + 8 * j + 4 * h]);
+          const h2 s01 = __builtin_bit_cast(h2, mw.x) * mx2;
+          const h2 s23 = __builtin_bit_cast(h2, mw.y) * mx2;
+          acc[it][4 * j + 0] = __builtin_fmaf(p[4 * j + 0], static_cast<float>(s01[0]), acc[it][4 * j + 0]);
+          acc[it][4 * j + 1] = __builtin_fmaf(p[4 * j + 1], static_cast<float>(s01[1]), acc[it][4 * j + 1]);
+          acc[it][4 * j + 2] = __builtin_fmaf(p[4 * j + 2], static_cast<float>(s23[0]), acc[it][4 * j + 2]);
+          acc[it][4 * j + 3] = __builtin_fmaf(p[4 * j + 3], static_cast<float>(s23[1]), acc[it][4 * j + 3]);
         }
       }
       // one tile's products in flight at a time (register budget)
@@ -390,27 +477,32 @@ __global__ __launch_bounds__(kK2Threads, 4) void k2_gemm_w4a4(
   ld.c = make_uint4(0, 0, 0, 0);
   ld.sc = 0;
   gload(0, ld);
-  lstore(0, ld);
+  lstore(Slot<0>{}, ld);
   if (G > 1) {
     gload(1, ld);
-    lstore(1, ld);
+    lstore(Slot<1>{}, ld);
   }
   __syncthreads();
 
-  // iteration g: issue the loads of g+2, compute g from LDS, store g+2 into
-  // the third slot, barrier.  Waves of the other workgroup on the CU run
-  // while this one waits for its loads.
-  for (int g = 0; g < G; ++g) {
-    if (g + 2 < G) gload(g + 2, ld);
-    compute(g);
-    if (g + 2 < G) lstore(g + 2, ld);
+  // iteration g: issue the loads of g+2, compute g from ring slot g%3,
+  // store g+2 into slot (g+2)%3, barrier.  Unrolled by the ring size so
+  // that every slot address is a compile-time offset.  Waves of the other
+  // workgroup on the CU run while this one waits for its loads.
+  auto iteration = [&](int g, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    const bool more = g + 2 < G;
+    if (more) gload(g + 2, ld);
+    compute(g, buf_c);
+    if (more) lstore(Slot<(buf + 2) % 3>{}, ld);
     __syncthreads();
+  };
+  for (int g = 0; g < G; g += 3) {
+    iteration(g, Slot<0>{});
+    if (g + 1 < G) iteration(g + 1, Slot<1>{});
+    if (g + 2 < G) iteration(g + 2, Slot<2>{});
   }
 
   if constexpr (!DEBUG) {
-#pragma unroll
-    for (int it = 0; it < 2; ++it) acc[it] *= 262144.0f;   // 2^18, exact
-
     // up projection: acc += bf16(lora_act) . L2 on the same tiles, K = 16
     // per v_mfma_f32_32x32x16_bf16 (rank is a multiple of 16)
     const int m = m0 + wm * 32 + l32;
@@ -476,10 +568,17 @@ hipError_t launch_k1(const void* x, int M, int K, const float* sinv, const void*
     if (waves > lds_cap) waves = lds_cap;
   }
   if (waves < 1) waves = 1;
-  const size_t lds = RT > 0 ? static_cast<size_t>(waves) * 16 * RT * 16 * sizeof(float) : 0;
+  const size_t red = RT > 0 ? static_cast<size_t>(waves) * 16 * RT * 16 * sizeof(float) : 0;
+  // smooth_inv goes to LDS while two workgroups still fit on a CU
+  const bool sinv_lds = red + static_cast<size_t>(K) * sizeof(float) <= 80 * 1024;
   dim3 grid((M + 15) / 16), block(64 * waves);
-  hipLaunchKernelGGL(k1_quant_down_int4<RT>, grid, block, lds, st, static_cast<const uint16_t*>(x), M, K, sinv,
-                     static_cast<const uint16_t*>(ldown), xq, static_cast<uint16_t*>(xs), lact);
+  if (sinv_lds)
+    hipLaunchKernelGGL((k1_quant_down_int4<RT, true>), grid, block, red + static_cast<size_t>(K) * sizeof(float), st,
+                       static_cast<const uint16_t*>(x), M, K, sinv, static_cast<const uint16_t*>(ldown), xq,
+                       static_cast<uint16_t*>(xs), lact);
+  else
+    hipLaunchKernelGGL((k1_quant_down_int4<RT, false>), grid, block, red, st, static_cast<const uint16_t*>(x), M, K,
+                       sinv, static_cast<const uint16_t*>(ldown), xq, static_cast<uint16_t*>(xs), lact);
   return hipGetLastError();
 }
 

@@ -156,6 +156,58 @@ def test_k2_parity(p):
     assert_y_close(host_u16(y), ref["y"], "k2")
 
 
+# scale regimes for the GEMM's exponent/significand split of s_w * s_x
+_SCALE_KINDS = ("subnormal", "huge", "mixed")
+
+
+def _scales(rng, kind, shape):
+    """fp16 scale arrays that span the format: zero, subnormal, normal and
+    the largest finite value, as bit patterns."""
+    if kind == "subnormal":
+        bits = rng.integers(1, 0x0400, size=shape)                       # 2^-24 .. just below 2^-14
+        bits[..., ::7] = 0x0001
+        bits[..., 3::11] = 0x03FF
+    elif kind == "huge":
+        bits = rng.integers(0x7000, 0x7C00, size=shape)                  # 2^13 .. 65504
+        bits[..., ::5] = 0x7BFF
+    else:
+        bits = rng.integers(0, 0x7C00, size=shape)                        # every finite positive value
+        bits[..., ::13] = 0x0000
+        bits[..., 1::17] = 0x0001
+        bits[..., 2::19] = 0x0400
+        bits[..., 3::23] = 0x7BFF
+    return bits.astype(np.uint16).view(np.float16)
+
+
+@pytest.mark.parametrize("kind", _SCALE_KINDS)
+@pytest.mark.parametrize("rank", [0, 16])
+def test_k2_scale_extremes(kind, rank):
+    """The GEMM on hand-made codes and scales across the whole fp16 range
+    (zero scales with non-zero codes included: their products are zero)."""
+    say(f"k2 scales {kind} rank {rank}")
+    rng = np.random.default_rng([77, rank, _SCALE_KINDS.index(kind)])
+    M, K, N = 131, 640, 140
+    G = K // 64
+    qx = rng.integers(-7, 8, size=(M, K))
+    qw = rng.integers(-7, 8, size=(N, K))
+    xq, wq = O.pack_int4(qx), O.pack_int4(qw)
+    xs, ws = _scales(rng, kind, (G, M)), _scales(rng, kind, (G, N))
+    t = rng.standard_normal((M, rank)).astype(np.float32)
+    l2 = O.f32_to_bf16_bits((rng.standard_normal((rank, N)) * 0.05).astype(np.float32))
+    bias = O.f32_to_bf16_bits((rng.standard_normal(N) * 0.01).astype(np.float32))
+    if kind == "subnormal":
+        # products near 2^-48: keep the output made of them alone
+        bias, t, l2 = None, t * 0, l2 * 0
+    ref = O.gemm_w4a4_lora_up(xq, xs, wq, ws, t.astype(np.float64), l2, bias)
+    y = bq.gemm_w4a4_lora_up(dev(xq), dev(xs), dev(wq), dev(ws), dev(t) if rank else None,
+                             dev_bf16(np.ascontiguousarray(l2.T)) if rank else None,
+                             None if bias is None else dev_bf16(bias), M, N, K, rank)
+    torch.cuda.synchronize()
+    yb = host_u16(y)
+    assert np.all(np.isfinite(O.bf16_bits_to_f32(yb)))
+    assert_y_close(yb, ref["y"], f"k2 scales {kind}")
+
+
 @pytest.mark.parametrize("p", SMALL, ids=lambda p: "M%dK%dN%dr%d" % p[:4])
 def test_layer_end_to_end(p):
     case = _small(p)
