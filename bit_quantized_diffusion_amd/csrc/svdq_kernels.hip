@@ -66,98 +66,102 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
 // ---------------------------------------------------------------------------
 // Kernel 1: smoothing + INT4 activation quantization + down projection.
 //
-// A workgroup owns 16 rows and all of K, with W waves (W = blockDim/64).  A
-// wave step covers the 16 rows x 2 groups (128 k): lane l owns row l % 16
-// and the 32 contiguous k at (l/16)*32, half of one group, read as 4 chunks
-// of 8 k.  The group absmax needs one lane exchange (the other half is 16
-// lanes away), and the lane's 32 codes leave as one 16-byte store.  X^ is
-// rounded to bf16 by v_cvt_pk_bf16_f32; chunk c of the 4 lanes of a row is
-// the A operand of one bf16 MFMA with L1 (K = 32: k at q*32 + c*8 + 0..7 for
-// lane group q; the L1 fragment is loaded with the same k), so X is read
-// once.  Waves take steps round-robin and their partial X^ L1 tiles are
-// summed in LDS in a fixed order (deterministic).
+// A workgroup of 4 waves owns 64 rows (16 per wave: one row tile of the
+// down projection's 16x16 MFMA) and one slice of K (a multiple of 128 k;
+// blockIdx.y).  A wave step covers its 16 rows x 128 k: lane l owns row
+// l % 16 and the 32 contiguous k at (l/16)*32, half of one group, read as 4
+// chunks of 8 k.  The group absmax needs one lane exchange (the other half
+// is 16 lanes away), and the lane's 32 codes leave as one 16-byte store.
+// X^ is rounded to bf16 by v_cvt_pk_bf16_f32; chunk c of the 4 lanes of a
+// row is the A operand of one bf16 MFMA with L1 (K = 32: k at q*32 + c*8 +
+// 0..7 for lane group q; the L1 fragment is loaded with the same k), so X is
+// read once.  The four waves of a workgroup read the same L1 fragments, so
+// the L1 (lora_down) traffic to L2 is that of 64 rows, not 16.
+//
+// With more than one K slice, each workgroup adds its 64 x rank partial
+// X^ L1 into lora_act with fp32 atomics (lora_act is cleared first by a
+// small fill kernel); the order of those additions is not fixed, so
+// lora_act can differ in its last bits between runs.  With one slice the
+// partial is stored directly.
 //
 // The kernel is bound by HBM reads of X, so every load is unconditional
 // (row and k clamped into the matrix; data of a clamped chunk is zeroed
 // before use, stores are predicated) and the X of a wave's next step is
-// requested before the current step is processed: a wave keeps a step of X
-// and the current step's L1 fragments in flight instead of one round trip
-// per load.
+// requested before the current step is processed.
 // ---------------------------------------------------------------------------
 
-template <int RT, bool SINV_LDS>
-__global__ __launch_bounds__(512, RT <= 2 ? 4 : 2) void k1_quant_down_int4(
+constexpr int kK1Rows = 64;       // rows per workgroup (4 waves x 16)
+
+template <int RT, bool ATOMIC>
+__global__ __launch_bounds__(256) void k1_quant_down_int4(
     const uint16_t* __restrict__ x, int M, int K, const float* __restrict__ sinv,
     const uint16_t* __restrict__ ldown, uint8_t* __restrict__ xq, uint16_t* __restrict__ xs,
-    float* __restrict__ lact) {
+    float* __restrict__ lact, int ks) {
   constexpr int RANK = RT * 16;
   constexpr int TB = RT < 2 ? (RT > 0 ? RT : 1) : 2;    // L1 fragments per batch of loads (ranks of 16)
-  extern __shared__ float red[];            // [W][16][RANK], then smooth_inv [K] when SINV_LDS
+  extern __shared__ float lds_sinv[];                   // smooth_inv of this workgroup's K slice
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int W = blockDim.x >> 6;
   const int r16 = lane & 15;
   const int q = lane >> 4;
-  const int row0 = blockIdx.x * 16;
+  const int row0 = blockIdx.x * kK1Rows + wave * 16;
   const int row = row0 + r16;
   const bool row_ok = row < M;
-  const int G = K / 64;
-  const int nsteps = (G + 1) / 2;
+  const int k_begin = blockIdx.y * ks;
+  const int k_end = min(K, k_begin + ks);
   const size_t xrow = static_cast<size_t>(row) * K;
   const uint16_t* xr = x + static_cast<size_t>(min(row, M - 1)) * K;
-  // k of chunk c of a step for this lane, clamped into the row
-  auto kof = [&](int step, int c) { return min(step * 128 + q * 32 + c * 8, K - 8); };
+  // k of chunk c of the step at kbase for this lane, clamped into the row
+  auto kof = [&](int kbase, int c) { return min(kbase + q * 32 + c * 8, K - 8); };
 
   v4f acc[RT > 0 ? RT : 1];
 #pragma unroll
   for (int t = 0; t < (RT > 0 ? RT : 1); ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // smooth_inv is read by every step of every wave: stage it in LDS once per
-  // workgroup so that its reads cost an LDS round trip, not an L2 one
-  float* const lds_sinv = red + (RT > 0 ? W * 16 * RANK : 0);
-  if constexpr (SINV_LDS) {
-    for (int i = threadIdx.x; i < K / 4; i += blockDim.x)
-      reinterpret_cast<float4*>(lds_sinv)[i] = reinterpret_cast<const float4*>(sinv)[i];
-    __syncthreads();
-  }
-  const float* const sv = SINV_LDS ? lds_sinv : sinv;
+  // smooth_inv is read by every step of every wave: stage the slice in LDS
+  for (int i = threadIdx.x; i < (k_end - k_begin) / 4; i += blockDim.x)
+    reinterpret_cast<float4*>(lds_sinv)[i] = reinterpret_cast<const float4*>(sinv + k_begin)[i];
+  __syncthreads();
+  // LDS copy of smooth_inv at k (k inside the slice; clamped k of the last
+  // chunk can fall 8 below the slice start only when the slice is the
+  // whole, shorter-than-128 row, and then it is still inside the slice)
+  auto sv = [&](int k) { return lds_sinv + (k - k_begin); };
 
   uint4 xn[4];
-  {
-    const int first = min(wave, nsteps - 1);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) xn[c] = *reinterpret_cast<const uint4*>(xr + kof(first, c));
-  }
+  for (int c = 0; c < 4; ++c) xn[c] = *reinterpret_cast<const uint4*>(xr + kof(k_begin, c));
+  auto load_l1 = [&](v4i (&dst)[4][TB], int kbase, int t0) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int t = 0; t < TB; ++t)
+        if (t0 + t < RT)
+          dst[c][t] = *reinterpret_cast<const v4i*>(ldown + static_cast<size_t>((t0 + t) * 16 + r16) * K + kof(kbase, c));
+  };
 
-  for (int step = wave; step < nsteps; step += W) {
-    const int kbase = step * 128;
+  for (int kbase = k_begin; kbase < k_end; kbase += 128) {
     uint4 xc[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) xc[c] = xn[c];
     {
-      const int nxt = min(step + W, nsteps - 1);        // the last step re-reads itself (unused)
+      const int nxt = kbase + 128 < k_end ? kbase + 128 : kbase;   // the last step re-reads itself (unused)
 #pragma unroll
       for (int c = 0; c < 4; ++c) xn[c] = *reinterpret_cast<const uint4*>(xr + kof(nxt, c));
     }
+    // lane (row, q) holds the 32 k at kbase + q*32: half of group
+    // kbase/64 + q/2, whose other half sits in lane q^1 (16 lanes away)
+    const bool valid = kbase + q * 32 < k_end;         // false only in a slice's odd last group
     float4 s0[4], s1[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      s0[c] = *reinterpret_cast<const float4*>(sv + kof(step, c));
-      s1[c] = *reinterpret_cast<const float4*>(sv + kof(step, c) + 4);
+      const int k = valid ? kbase + q * 32 + c * 8 : k_begin;
+      s0[c] = *reinterpret_cast<const float4*>(sv(k));
+      s1[c] = *reinterpret_cast<const float4*>(sv(k) + 4);
     }
     // first batch of L1 fragments, in flight during the quantization
     v4i lb[4][TB];
-    if constexpr (RT > 0) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int t = 0; t < TB; ++t)
-          lb[c][t] = *reinterpret_cast<const v4i*>(ldown + static_cast<size_t>(t * 16 + r16) * K + kof(step, c));
-    }
+    if constexpr (RT > 0) load_l1(lb, kbase, 0);
 
-    // lane (row, q) holds the 32 k at kbase + q*32: half of group
-    // step*2 + q/2, whose other half sits in lane q^1 (16 lanes away)
-    const bool valid = kbase + q * 32 < K;             // false only in the odd last group
     float xh[4][8];
     uint32_t pk[4][4];
 #pragma unroll
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(512, RT <= 2 ? 4 : 2) void k1_quant_down_int4(
     }
 
     {
-      const int g = step * 2 + (q >> 1);
+      const int g = kbase / 64 + (q >> 1);
       float amax = 0.f;
 #pragma unroll
       for (int c = 0; c < 4; ++c)
@@ -208,15 +212,7 @@ __global__ __launch_bounds__(512, RT <= 2 ? 4 : 2) void k1_quant_down_int4(
     if constexpr (RT > 0) {
 #pragma unroll
       for (int t0 = 0; t0 < RT; t0 += TB) {
-        if (t0 > 0) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int t = 0; t < TB; ++t)
-              if (t0 + t < RT)
-                lb[c][t] = *reinterpret_cast<const v4i*>(ldown + static_cast<size_t>((t0 + t) * 16 + r16) * K +
-                                                         kof(step, c));
-        }
+        if (t0 > 0) load_l1(lb, kbase, t0);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const v8bf a = __builtin_bit_cast(v8bf, (v4i{static_cast<int>(pk[c][0]), static_cast<int>(pk[c][1]),
@@ -232,18 +228,26 @@ __global__ __launch_bounds__(512, RT <= 2 ? 4 : 2) void k1_quant_down_int4(
   }
 
   if constexpr (RT > 0) {
+    // D layout: lane (q, r16), element i -> row 4q + i, column r16 of tile t
 #pragma unroll
     for (int t = 0; t < RT; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[(wave * 16 + 4 * q + i) * RANK + t * 16 + r16] = acc[t][i];
-    __syncthreads();
-    for (int e = threadIdx.x; e < 16 * RANK; e += blockDim.x) {
-      const int rr = e / RANK;
-      float sum = red[e];
-      for (int w2 = 1; w2 < W; ++w2) sum += red[w2 * 16 * RANK + e];
-      if (row0 + rr < M) lact[static_cast<size_t>(row0 + rr) * RANK + (e - rr * RANK)] = sum;
-    }
+      for (int i = 0; i < 4; ++i) {
+        const int rr = row0 + 4 * q + i;
+        if (rr < M) {
+          float* dst = lact + static_cast<size_t>(rr) * RANK + t * 16 + r16;
+          if constexpr (ATOMIC)
+            atomicAdd(dst, acc[t][i]);
+          else
+            *dst = acc[t][i];
+        }
+      }
   }
+}
+
+__global__ void fill_zero_f32(float* __restrict__ p, size_t n) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -557,28 +561,32 @@ __global__ __launch_bounds__(kK2Threads, 4) void k2_gemm_w4a4(
   }
 }
 
+// K1 grid: 64-row blocks x K slices.  The slice count is chosen so that
+// the grid holds about four workgroups per CU (256 CUs), with slices of
+// whole 128-k steps.
 template <int RT>
 hipError_t launch_k1(const void* x, int M, int K, const float* sinv, const void* ldown, uint8_t* xq, void* xs,
                      float* lact, hipStream_t st) {
-  const int G = K / 64;
-  const int nsteps = (G + 1) / 2;
-  int waves = nsteps < 8 ? nsteps : 8;
-  if constexpr (RT > 0) {
-    const int lds_cap = 1024 / (RT * 16);     // W * 16 * RANK * 4 bytes <= 64 KiB
-    if (waves > lds_cap) waves = lds_cap;
+  const int row_blocks = (M + kK1Rows - 1) / kK1Rows;
+  const int steps = (K + 127) / 128;
+  int slices = (1024 + row_blocks - 1) / row_blocks;
+  if (slices > steps) slices = steps;
+  if (slices < 1) slices = 1;
+  const int steps_per_slice = (steps + slices - 1) / slices;
+  const int ks = steps_per_slice * 128;
+  slices = (steps + steps_per_slice - 1) / steps_per_slice;
+  const size_t lds = static_cast<size_t>(ks) * sizeof(float);
+  dim3 grid(row_blocks, slices), block(256);
+  const bool atomic = RT > 0 && slices > 1;
+  if (atomic) {
+    const size_t n = static_cast<size_t>(M) * RT * 16;
+    hipLaunchKernelGGL(fill_zero_f32, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, lact, n);
+    hipLaunchKernelGGL((k1_quant_down_int4<RT, true>), grid, block, lds, st, static_cast<const uint16_t*>(x), M, K,
+                       sinv, static_cast<const uint16_t*>(ldown), xq, static_cast<uint16_t*>(xs), lact, ks);
+  } else {
+    hipLaunchKernelGGL((k1_quant_down_int4<RT, false>), grid, block, lds, st, static_cast<const uint16_t*>(x), M, K,
+                       sinv, static_cast<const uint16_t*>(ldown), xq, static_cast<uint16_t*>(xs), lact, ks);
   }
-  if (waves < 1) waves = 1;
-  const size_t red = RT > 0 ? static_cast<size_t>(waves) * 16 * RT * 16 * sizeof(float) : 0;
-  // smooth_inv goes to LDS while two workgroups still fit on a CU
-  const bool sinv_lds = red + static_cast<size_t>(K) * sizeof(float) <= 80 * 1024;
-  dim3 grid((M + 15) / 16), block(64 * waves);
-  if (sinv_lds)
-    hipLaunchKernelGGL((k1_quant_down_int4<RT, true>), grid, block, red + static_cast<size_t>(K) * sizeof(float), st,
-                       static_cast<const uint16_t*>(x), M, K, sinv, static_cast<const uint16_t*>(ldown), xq,
-                       static_cast<uint16_t*>(xs), lact);
-  else
-    hipLaunchKernelGGL((k1_quant_down_int4<RT, false>), grid, block, red, st, static_cast<const uint16_t*>(x), M, K,
-                       sinv, static_cast<const uint16_t*>(ldown), xq, static_cast<uint16_t*>(xs), lact);
   return hipGetLastError();
 }
 
