@@ -60,6 +60,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--sets", type=int, default=4, help="rotated buffer sets")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-ablation", action="store_true",
+                   help="skip the fused-vs-unfused (four kernel) comparison")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="time budget of the oracle sample (whole chunks of rows)")
     p.add_argument("--cpu-chunk", type=int, default=96, help="token rows per oracle chunk")
@@ -228,6 +230,10 @@ def main():
                 "traffic_source": TRAFFIC_NOTE if traffic is not None else
                 ("counter summary taken on older kernel source" if traffic_state == "stale" else None)}
 
+    ablation = None
+    if not args.no_ablation:
+        ablation = fusion_ablation(bq, torch, np, sets, M, (s1, s2), per, stream, reps=10)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(lay1, pk1, s1, args.cpu_seconds, args.cpu_chunk)
@@ -243,8 +249,54 @@ def main():
         "us_per_layer": {k: v["us_layer"] for k, v in per.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "fusion_ablation": ablation,
     }
     print(json.dumps(out), flush=True)
+
+
+def layer_bytes(M, K, N, r, bias=True):
+    """Algorithmic HBM bytes of one layer: fused (two kernels) and unfused
+    (quantize, down projection, 4-bit GEMM, up projection)."""
+    x, sinv, l1, l2 = M * K * 2, K * 4, r * K * 2, N * r * 2
+    xq, xs, wq, ws, la = M * K // 2, (K // 64) * M * 2, N * K // 2, (K // 64) * N * 2, M * r * 4
+    b, y = (N * 2 if bias else 0), M * N * 2
+    k1 = x + sinv + l1 + xq + xs + la
+    k2 = xq + xs + wq + ws + la + l2 + b + y
+    quant = x + sinv + xq + xs
+    down = x + sinv + l1 + la
+    gemm = xq + xs + wq + ws + y
+    up = la + l2 + b + y + y
+    return k1 + k2, quant + down + gemm + up
+
+
+def fusion_ablation(bq, torch, np, sets, M, specs, per, stream, reps):
+    """Times the unfused four-kernel layer on the same buffers as the fused
+    one (outside the timed step), next to the fused per-layer times."""
+    out = {}
+    for li, (tag, s) in enumerate(zip(("fc1", "fc2"), specs)):
+        for i in range(3):
+            b = sets[i % len(sets)][li]
+            bq.unfused_linear(b["x"], b["L"], y=b["y"], xq=b["xq"], xs=b["xs"], lora_act=b["la"])
+        torch.cuda.synchronize()
+        evs = []
+        for i in range(reps):
+            b = sets[i % len(sets)][li]
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            bq.unfused_linear(b["x"], b["L"], y=b["y"], xq=b["xq"], xs=b["xs"], lora_act=b["la"])
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        us_unfused = 1e3 * float(np.mean([a.elapsed_time(c) for a, c in evs]))
+        fused_b, unfused_b = layer_bytes(s.M, s.K, s.N, s.rank)
+        us_fused = per[tag]["us_layer"]
+        out[tag] = {"us_fused": us_fused, "us_unfused": round(us_unfused, 2),
+                    "unfused_over_fused": round(us_unfused / us_fused, 3),
+                    "algorithmic_mb_fused": round(fused_b / 1e6, 1),
+                    "algorithmic_mb_unfused": round(unfused_b / 1e6, 1),
+                    "mb_saved_by_fusion": round((unfused_b - fused_b) / 1e6, 1)}
+    log(f"bench: fusion ablation {json.dumps(out)}")
+    return out
 
 
 def cpu_baseline(lay1, pk1, spec, seconds, chunk):

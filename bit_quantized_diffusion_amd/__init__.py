@@ -27,7 +27,7 @@ from ._lib import (INT4, MXFP4, SVDQ_ERR_HIP, SVDQ_ERR_INVALID_ARG,  # noqa: F40
 __all__ = [
     "INT4", "MXFP4", "SvdqError", "lib", "LIB_PATH", "status_string",
     "version", "device_check", "packed_sizes", "act_sizes", "pack_weights",
-    "quantize_act_lora_down", "gemm_w4a4_lora_up", "debug_group_partials",
+    "quantize_act_lora_down", "gemm_w4a4_lora_up", "debug_group_partials", "unfused_linear",
     "PackedLinear", "linear",
 ]
 
@@ -170,6 +170,34 @@ def gemm_w4a4_lora_up(xq, xs, wq, ws, lora_act, lora_up, bias, M: int, N: int, K
         _dptr(bias, torch.bfloat16, (N,), "bias"),
         _dptr(y, torch.bfloat16, (M, N), "y"),
         M, N, K, rank, precision, _stream(dev)))
+    return y
+
+
+def unfused_linear(x, layer: "PackedLinear", y=None, xq=None, xs=None, lora_act=None):
+    """The same layer as four separate kernels (quantize, down projection,
+    4-bit GEMM, up projection): the baseline the two fusions are measured
+    against.  INT4 only.  Returns y bf16 [M][N]."""
+    torch = _torch()
+    M, K = x.shape
+    N, r, dev = layer.N, layer.rank, x.device
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if xq is None:
+        xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    if xs is None:
+        xs = torch.empty((K // 64, M), dtype=torch.float16, device=dev)
+    if r and lora_act is None:
+        lora_act = torch.empty((M, r), dtype=torch.float32, device=dev)
+    check(lib.svdq_unfused_linear(
+        _dptr(x, torch.bfloat16, (M, K), "x"), M, K,
+        _dptr(layer.smooth_inv, torch.float32, (K,), "smooth_inv"),
+        _dptr(layer.lora_down, torch.bfloat16, (r, K), "lora_down") if r else None, r,
+        _dptr(layer.wq, torch.uint8, (N, K // 2), "wq"), _dptr(layer.ws, torch.float16, (K // 64, N), "ws"),
+        _dptr(layer.lora_up, torch.bfloat16, (N, r), "lora_up") if r else None,
+        _dptr(layer.bias, torch.bfloat16, (N,), "bias"), N, layer.precision,
+        _dptr(xq, torch.uint8, (M, K // 2), "xq"), _dptr(xs, torch.float16, (K // 64, M), "xs"),
+        _dptr(lora_act, torch.float32, (M, r), "lora_act") if r else None,
+        _dptr(y, torch.bfloat16, (M, N), "y"), _stream(dev)))
     return y
 
 

@@ -25,7 +25,7 @@ EXPORTED = (
     "svdq_version", "svdq_status_string", "svdq_device_check",
     "svdq_packed_sizes", "svdq_act_sizes", "svdq_pack_weights",
     "svdq_quantize_act_lora_down", "svdq_gemm_w4a4_lora_up",
-    "svdq_debug_group_partials",
+    "svdq_unfused_linear", "svdq_debug_group_partials",
 )
 
 
@@ -39,7 +39,7 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with "
-            "`python -m bit_quantized_diffusion_amd.build` (hipcc, gfx950)")
+            "`python bit_quantized_diffusion_amd/build.py` (hipcc, gfx950)")
     # The tensors handed to the library come from torch, which ships its own
     # HIP runtime.  Load torch first so that libsvdq.so binds to that same
     # runtime (the dynamic loader reuses the already loaded libamdhip64);
@@ -57,6 +57,7 @@ def _load():
         "svdq_pack_weights": ([vp, vp, i, i, i, i, vp, vp, vp, vp, vp, vp], i),
         "svdq_quantize_act_lora_down": ([vp, i, i, vp, vp, i, i, vp, vp, vp, vp], i),
         "svdq_gemm_w4a4_lora_up": ([vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp], i),
+        "svdq_unfused_linear": ([vp, i, i, vp, vp, i, vp, vp, vp, vp, i, i, vp, vp, vp, vp, vp], i),
         "svdq_debug_group_partials": ([vp, vp, i, i, i, i, i, i, i, vp, vp], i),
     }
     for name, (args, ret) in sig.items():

@@ -1,6 +1,9 @@
 """Build libsvdq.so in-tree with hipcc for gfx950.
 
-    python -m bit_quantized_diffusion_amd.build [-v]
+    python bit_quantized_diffusion_amd/build.py [-v]
+
+(run as a file: importing the package needs a library that is already
+built)
 
 The kernels are compiled for gfx950 only.  Packed-FP32 VALU instructions are
 disabled (-packed-fp32-ops) and no fast-math flag is used: the quantizer

@@ -144,6 +144,27 @@ int svdq_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs, const uint8_t* wq,
                                                   precision, stream));
 }
 
+int svdq_unfused_linear(const void* x, int M, int K, const float* smooth_inv, const void* lora_down, int rank,
+                        const uint8_t* wq, const void* ws, const void* lora_up, const void* bias, int N,
+                        int precision, uint8_t* xq, void* xs, float* lora_act, void* y, void* stream) {
+  int st = check_precision(precision);
+  if (st) return st;
+  if (!x || !smooth_inv || !wq || !ws || !xq || !xs || !y) return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!lora_down || !lora_up || !lora_act)) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(smooth_inv) || !aligned16(wq) || !aligned16(ws) || !aligned16(xq) ||
+      !aligned16(xs) || !aligned16(y))
+    return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!aligned16(lora_down) || !aligned16(lora_up) || !aligned16(lora_act))) return SVDQ_ERR_INVALID_ARG;
+  if (bias && !aligned16(bias)) return SVDQ_ERR_INVALID_ARG;
+  if (M < 1 || N < 1) return SVDQ_ERR_SHAPE;
+  if ((st = check_k(K, precision))) return st;
+  if ((st = check_rank(rank, K, N))) return st;
+  if (precision != SVDQ_INT4) return SVDQ_ERR_INVALID_ARG;
+  if ((st = current_device_ok())) return st;
+  return hip_status(svdq_launch_unfused_linear(x, M, K, smooth_inv, lora_down, rank, wq, ws, lora_up, bias, N,
+                                               precision, xq, xs, lora_act, y, stream));
+}
+
 int svdq_debug_group_partials(const uint8_t* xq, const uint8_t* wq, int M, int N, int K, int m0, int n0, int mt,
                               int nt, int32_t* out, void* stream) {
   if (!xq || !wq || !out) return SVDQ_ERR_INVALID_ARG;

@@ -43,6 +43,12 @@ int svdq_launch_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs,
                                   const void* bias, void* y, int M, int N,
                                   int K, int rank, int precision,
                                   void* stream);
+int svdq_launch_unfused_linear(const void* x, int M, int K,
+                               const float* smooth_inv, const void* lora_down,
+                               int rank, const uint8_t* wq, const void* ws,
+                               const void* lora_up, const void* bias, int N,
+                               int precision, uint8_t* xq, void* xs,
+                               float* lora_act, void* y, void* stream);
 int svdq_launch_debug_group_partials(const uint8_t* xq, const uint8_t* wq,
                                      int M, int N, int K, int m0, int n0,
                                      int mt, int nt, int32_t* out,

@@ -92,7 +92,7 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
 
 constexpr int kK1Rows = 64;       // rows per workgroup (4 waves x 16)
 
-template <int RT, bool ATOMIC>
+template <int RT, bool ATOMIC, bool QUANT = true>
 __global__ __launch_bounds__(256) void k1_quant_down_int4(
     const uint16_t* __restrict__ x, int M, int K, const float* __restrict__ sinv,
     const uint16_t* __restrict__ ldown, uint8_t* __restrict__ xq, uint16_t* __restrict__ xs,
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256) void k1_quant_down_int4(
       }
     }
 
-    {
+    if constexpr (QUANT) {
       const int g = kbase / 64 + (q >> 1);
       float amax = 0.f;
 #pragma unroll
@@ -564,7 +564,7 @@ __global__ __launch_bounds__(kK2Threads, 4) void k2_gemm_w4a4(
 // K1 grid: 64-row blocks x K slices.  The slice count is chosen so that
 // the grid holds about four workgroups per CU (256 CUs), with slices of
 // whole 128-k steps.
-template <int RT>
+template <int RT, bool QUANT = true>
 hipError_t launch_k1(const void* x, int M, int K, const float* sinv, const void* ldown, uint8_t* xq, void* xs,
                      float* lact, hipStream_t st) {
   const int row_blocks = (M + kK1Rows - 1) / kK1Rows;
@@ -581,12 +581,106 @@ hipError_t launch_k1(const void* x, int M, int K, const float* sinv, const void*
   if (atomic) {
     const size_t n = static_cast<size_t>(M) * RT * 16;
     hipLaunchKernelGGL(fill_zero_f32, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, lact, n);
-    hipLaunchKernelGGL((k1_quant_down_int4<RT, true>), grid, block, lds, st, static_cast<const uint16_t*>(x), M, K,
+    hipLaunchKernelGGL((k1_quant_down_int4<RT, true, QUANT>), grid, block, lds, st, static_cast<const uint16_t*>(x), M, K,
                        sinv, static_cast<const uint16_t*>(ldown), xq, static_cast<uint16_t*>(xs), lact, ks);
   } else {
-    hipLaunchKernelGGL((k1_quant_down_int4<RT, false>), grid, block, lds, st, static_cast<const uint16_t*>(x), M, K,
+    hipLaunchKernelGGL((k1_quant_down_int4<RT, false, QUANT>), grid, block, lds, st, static_cast<const uint16_t*>(x), M, K,
                        sinv, static_cast<const uint16_t*>(ldown), xq, static_cast<uint16_t*>(xs), lact, ks);
   }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Unfused baseline (engine caption (a) of the "svdq-int4-flux.1-dev" card:
+// the low-rank branch as separate kernels): quantize (K1 without the down
+// projection), down projection (K1's loop without the quantizer, reading X a
+// second time), 4-bit GEMM (K2 without the up projection and bias, writing
+// a bf16 Y) and this up projection, which reads Y back, adds
+// bf16(lora_act) . L2 and the bias, and writes Y again.  Same arithmetic as
+// the fused path except that the GEMM's output is rounded to bf16 before the
+// up projection is added (a second rounding).
+//
+// Tile 64 (n) x 64 (m) per workgroup of 4 waves, 32 x 32 per wave, Y^T
+// orientation as in kernel 2 (a lane holds 4 consecutive channels of one
+// token: 8-byte loads and stores of Y).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_up_proj(const float* __restrict__ lact, const uint16_t* __restrict__ lup,
+                                                 const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M,
+                                                 int N, int rank) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int n0 = blockIdx.x * 64 + (wave & 1) * 32;
+  const int m0 = blockIdx.y * 64 + (wave >> 1) * 32;
+  const int m = m0 + l32, n = n0 + l32;
+  v16f acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  for (int c0 = 0; c0 < rank; c0 += 16) {
+    const int j = c0 + 8 * h;
+    v4i ub = v4i{0, 0, 0, 0}, ua = v4i{0, 0, 0, 0};
+    if (m < M) {
+      const float4* src = reinterpret_cast<const float4*>(lact + static_cast<size_t>(m) * rank + j);
+      const float4 f0 = src[0], f1 = src[1];
+      ub = v4i{static_cast<int>(pack_bf16_rne(f0.x, f0.y)), static_cast<int>(pack_bf16_rne(f0.z, f0.w)),
+               static_cast<int>(pack_bf16_rne(f1.x, f1.y)), static_cast<int>(pack_bf16_rne(f1.z, f1.w))};
+    }
+    if (n < N) ua = *reinterpret_cast<const v4i*>(lup + static_cast<size_t>(n) * rank + j);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ua), __builtin_bit_cast(v8bf, ub), acc, 0,
+                                                  0, 0);
+  }
+  float out[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    out[r] = acc[r];
+    asm volatile("" : "+v"(out[r]));     // read the MFMA result before the predicated code below
+  }
+  if (m >= M) return;
+  const bool vec_ok = (N % 4) == 0;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int nb = n0 + 8 * jj + 4 * h;
+    uint16_t* dst = y + static_cast<size_t>(m) * N + nb;
+    if (vec_ok && nb + 3 < N) {
+      const uint2 old = *reinterpret_cast<const uint2*>(dst);
+      const uint32_t ov[4] = {old.x & 0xFFFFu, old.x >> 16, old.y & 0xFFFFu, old.y >> 16};
+      uint32_t nv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float b = bias ? __uint_as_float(static_cast<uint32_t>(bias[nb + i]) << 16) : 0.f;
+        nv[i] = bf16_rne_bits(__uint_as_float(ov[i] << 16) + out[4 * jj + i] + b);
+      }
+      *reinterpret_cast<uint2*>(dst) = make_uint2(nv[0] | (nv[1] << 16), nv[2] | (nv[3] << 16));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (nb + i < N) {
+          const float b = bias ? __uint_as_float(static_cast<uint32_t>(bias[nb + i]) << 16) : 0.f;
+          dst[i] = static_cast<uint16_t>(bf16_rne_bits(__uint_as_float(static_cast<uint32_t>(dst[i]) << 16) +
+                                                       out[4 * jj + i] + b));
+        }
+    }
+  }
+}
+
+template <int RT>
+hipError_t launch_unfused(const void* x, int M, int K, const float* sinv, const void* ldown, const uint8_t* wq,
+                          const void* ws, const void* lup, const void* bias, int N, uint8_t* xq, void* xs,
+                          float* lact, void* y, hipStream_t st) {
+  hipError_t e = launch_k1<0>(x, M, K, sinv, nullptr, xq, xs, nullptr, st);           // 1: quantize
+  if (e != hipSuccess) return e;
+  if constexpr (RT > 0) {
+    e = launch_k1<RT, false>(x, M, K, sinv, ldown, xq, xs, lact, st);                 // 2: down projection
+    if (e != hipSuccess) return e;
+  }
+  const int tiles = ((N + kTile - 1) / kTile) * ((M + kTile - 1) / kTile);               // 3: 4-bit GEMM
+  hipLaunchKernelGGL(k2_gemm_w4a4<false>, dim3(tiles), dim3(kK2Threads), 0, st, xq,
+                     static_cast<const uint16_t*>(xs), wq, static_cast<const uint16_t*>(ws), nullptr, nullptr,
+                     nullptr, static_cast<uint16_t*>(y), M, N, K, 0, 0, 0, 0, 0, nullptr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_up_proj, dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, st, lact,  // 4: up projection
+                     static_cast<const uint16_t*>(lup), static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y),
+                     M, N, RT * 16);
   return hipGetLastError();
 }
 
@@ -623,6 +717,28 @@ extern "C" int svdq_launch_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs, 
                      static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias),
                      static_cast<uint16_t*>(y), M, N, K, rank, 0, 0, 0, 0, nullptr);
   return static_cast<int>(hipGetLastError());
+}
+
+extern "C" int svdq_launch_unfused_linear(const void* x, int M, int K, const float* smooth_inv, const void* lora_down,
+                                          int rank, const uint8_t* wq, const void* ws, const void* lora_up,
+                                          const void* bias, int N, int precision, uint8_t* xq, void* xs,
+                                          float* lora_act, void* y, void* stream) {
+  if (precision != SVDQ_INT4) return static_cast<int>(hipErrorInvalidValue);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (rank / 16) {
+#define SVDQ_UF_CASE(R) \
+  case R:               \
+    e = launch_unfused<R>(x, M, K, smooth_inv, lora_down, wq, ws, lora_up, bias, N, xq, xs, lora_act, y, st); \
+    break;
+    SVDQ_UF_CASE(0) SVDQ_UF_CASE(1) SVDQ_UF_CASE(2) SVDQ_UF_CASE(3) SVDQ_UF_CASE(4) SVDQ_UF_CASE(5)
+    SVDQ_UF_CASE(6) SVDQ_UF_CASE(7) SVDQ_UF_CASE(8) SVDQ_UF_CASE(9) SVDQ_UF_CASE(10) SVDQ_UF_CASE(11)
+    SVDQ_UF_CASE(12) SVDQ_UF_CASE(13) SVDQ_UF_CASE(14) SVDQ_UF_CASE(15) SVDQ_UF_CASE(16)
+#undef SVDQ_UF_CASE
+    default:
+      return static_cast<int>(hipErrorInvalidValue);
+  }
+  return static_cast<int>(e);
 }
 
 extern "C" int svdq_launch_debug_group_partials(const uint8_t* xq, const uint8_t* wq, int M, int N, int K, int m0,

@@ -162,6 +162,23 @@ SVDQ_API int svdq_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs,
                            int M, int N, int K, int rank, int precision,
                            void* stream);
 
+/* Unfused baseline of the same layer, for measuring what the two fusions
+ * save (model card "svdq-int4-flux.1-dev", Nunchaku engine caption (a): a
+ * naive low-rank branch as separate kernels costs an extra 16-bit read of
+ * X in the down projection and an extra 16-bit write of Y in the up
+ * projection).  Four kernels on `stream`: quantize (writes xq, xs),
+ * down projection (reads X again, writes lora_act), 4-bit GEMM (writes Y
+ * in bf16) and up projection (reads Y, adds bf16(lora_act) L2 and the
+ * bias, writes Y).  Arguments, layouts and errors as for the two fused
+ * calls; xq, xs and lora_act are caller-owned intermediates.  Results equal
+ * the fused path's up to the second bf16 rounding of Y.  INT4 only. */
+SVDQ_API int svdq_unfused_linear(const void* x, int M, int K,
+                        const float* smooth_inv, const void* lora_down, int rank,
+                        const uint8_t* wq, const void* ws,
+                        const void* lora_up, const void* bias, int N, int precision,
+                        uint8_t* xq, void* xs, float* lora_act, void* y,
+                        void* stream);
+
 /* Test hook: the exact per-group integer partials of the INT4 GEMM for the
  * output window rows [m0, m0+mt) x columns [n0, n0+nt), computed by the
  * same device code as svdq_gemm_w4a4_lora_up.

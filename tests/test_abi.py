@@ -83,6 +83,10 @@ def test_hot_calls_reject_null_and_misaligned():
     assert L.svdq_gemm_w4a4_lora_up(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, MIS, FAKE, 16, 16, 64, 16, 0, None) == bq.SVDQ_ERR_INVALID_ARG
     assert L.svdq_gemm_w4a4_lora_up(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 16, 16, 64, 16, 0, None) == bq.SVDQ_ERR_INVALID_ARG
     assert L.svdq_debug_group_partials(FAKE, None, 16, 16, 64, 0, 0, 1, 1, FAKE, None) == bq.SVDQ_ERR_INVALID_ARG
+    uf = L.svdq_unfused_linear
+    assert uf(None, 16, 64, FAKE, FAKE, 16, FAKE, FAKE, FAKE, None, 16, 0, FAKE, FAKE, FAKE, FAKE, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert uf(FAKE, 16, 64, FAKE, FAKE, 16, FAKE, FAKE, None, None, 16, 0, FAKE, FAKE, FAKE, FAKE, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert uf(FAKE, 16, 64, FAKE, FAKE, 16, FAKE, FAKE, FAKE, MIS, 16, 0, FAKE, FAKE, FAKE, FAKE, None) == bq.SVDQ_ERR_INVALID_ARG
 
 
 def test_hot_calls_reject_bad_shapes():
@@ -92,6 +96,10 @@ def test_hot_calls_reject_bad_shapes():
     assert L.svdq_quantize_act_lora_down(FAKE, 16, 64, FAKE, FAKE, 24, 0, FAKE, FAKE, FAKE, None) == bq.SVDQ_ERR_SHAPE
     assert L.svdq_gemm_w4a4_lora_up(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 16, 0, 64, 16, 0, None) == bq.SVDQ_ERR_SHAPE
     assert L.svdq_gemm_w4a4_lora_up(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 16, 8, 64, 16, 0, None) == bq.SVDQ_ERR_SHAPE
+    uf = L.svdq_unfused_linear
+    assert uf(FAKE, 16, 64, FAKE, FAKE, 16, FAKE, FAKE, FAKE, None, 0, 0, FAKE, FAKE, FAKE, FAKE, None) == bq.SVDQ_ERR_SHAPE
+    assert uf(FAKE, 16, 100, FAKE, FAKE, 16, FAKE, FAKE, FAKE, None, 16, 0, FAKE, FAKE, FAKE, FAKE, None) == bq.SVDQ_ERR_SHAPE
+    assert uf(FAKE, 16, 64, FAKE, FAKE, 24, FAKE, FAKE, FAKE, None, 16, 0, FAKE, FAKE, FAKE, FAKE, None) == bq.SVDQ_ERR_SHAPE
     # window outside the matrix
     assert L.svdq_debug_group_partials(FAKE, FAKE, 16, 16, 64, 10, 0, 7, 1, FAKE, None) == bq.SVDQ_ERR_SHAPE
 

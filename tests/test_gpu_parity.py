@@ -219,6 +219,27 @@ def test_layer_end_to_end(p):
     assert_y_close(host_u16(y), ref["y"], "layer")
 
 
+@pytest.mark.parametrize("p", SMALL, ids=lambda p: "M%dK%dN%dr%d" % p[:4])
+def test_unfused_baseline(p):
+    """The four-kernel baseline computes the same layer: against the oracle
+    to the same tolerance (its Y is rounded to bf16 twice), and its codes
+    and scales are the fused path's bit for bit."""
+    case = _small(p)
+    say(f"unfused {p}")
+    M = case["x"].shape[0]
+    ref = C.oracle_rows(case, np.arange(M))
+    layer = device_layer(case)
+    x = dev_bf16(case["x"])
+    y = bq.unfused_linear(x, layer)
+    xq, xs, _ = bq.quantize_act_lora_down(x, layer.smooth_inv, layer.lora_down, layer.rank)
+    xq_u = torch.empty_like(xq)
+    xs_u = torch.empty_like(xs)
+    bq.unfused_linear(x, layer, xq=xq_u, xs=xs_u)
+    torch.cuda.synchronize()
+    assert torch.equal(xq, xq_u) and torch.equal(xs.view(torch.int16), xs_u.view(torch.int16))
+    assert_y_close(host_u16(y), ref["y"], "unfused")
+
+
 def test_outputs_reused_buffers_and_streams():
     """Caller-owned outputs are written in place; a side stream works."""
     case = _small(SMALL[1])
