@@ -74,8 +74,7 @@ def pack_weights(w_bf16: np.ndarray, act_absmax: np.ndarray, rank: int,
         lora_down=np.empty((rank, K), np.uint16),
         lora_up=np.empty((N, rank), np.uint16),
         wq=np.empty((N, K // 2), np.uint8),
-        ws=(np.empty((K // 64, N), np.float16) if precision == INT4
-            else np.empty((K // 32, N), np.uint8)),
+        ws=np.empty(_scale_shape(K, N, precision), np.float16 if precision == INT4 else np.uint8),
     )
     r = np.empty((K, N), np.float32) if want_residual else None
     check(lib.svdq_pack_weights(
@@ -123,22 +122,24 @@ def _scale_dtype(precision):
     return torch.float16 if precision == INT4 else torch.uint8
 
 
-def _groups(K, precision):
-    return K // 64 if precision == INT4 else K // 32
+def _scale_shape(K, rows, precision):
+    """Scales are group-major: [K/64][rows] (INT4), [K/32][rows] (MXFP4)."""
+    return (K // 64, rows) if precision == INT4 else (K // 32, rows)
 
 
 def quantize_act_lora_down(x, smooth_inv, lora_down, rank: int, precision: int = INT4,
                            xq=None, xs=None, lora_act=None):
     """First fused kernel.  x: bf16 [M][K]; smooth_inv: f32 [K];
     lora_down: bf16 [rank][K] or None when rank == 0.
-    Returns (xq u8 [M][K/2], xs [K/g][M], lora_act f32 [M][rank] or None)."""
+    Returns (xq u8 [M][K/2], xs (INT4 [K/64][M] f16, MXFP4 [K/32][M] u8),
+    lora_act f32 [M][rank] or None)."""
     torch = _torch()
     M, K = x.shape
     dev = x.device
     if xq is None:
         xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
     if xs is None:
-        xs = torch.empty((_groups(K, precision), M), dtype=_scale_dtype(precision), device=dev)
+        xs = torch.empty(_scale_shape(K, M, precision), dtype=_scale_dtype(precision), device=dev)
     if rank and lora_act is None:
         lora_act = torch.empty((M, rank), dtype=torch.float32, device=dev)
     check(lib.svdq_quantize_act_lora_down(
@@ -147,7 +148,7 @@ def quantize_act_lora_down(x, smooth_inv, lora_down, rank: int, precision: int =
         _dptr(lora_down, torch.bfloat16, (rank, K), "lora_down") if rank else None,
         rank, precision,
         _dptr(xq, torch.uint8, (M, K // 2), "xq"),
-        _dptr(xs, _scale_dtype(precision), (_groups(K, precision), M), "xs"),
+        _dptr(xs, _scale_dtype(precision), _scale_shape(K, M, precision), "xs"),
         _dptr(lora_act, torch.float32, (M, rank), "lora_act") if rank else None,
         _stream(dev)))
     return xq, xs, (lora_act if rank else None)
@@ -161,10 +162,9 @@ def gemm_w4a4_lora_up(xq, xs, wq, ws, lora_act, lora_up, bias, M: int, N: int, K
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     sd = _scale_dtype(precision)
-    G = _groups(K, precision)
     check(lib.svdq_gemm_w4a4_lora_up(
-        _dptr(xq, torch.uint8, (M, K // 2), "xq"), _dptr(xs, sd, (G, M), "xs"),
-        _dptr(wq, torch.uint8, (N, K // 2), "wq"), _dptr(ws, sd, (G, N), "ws"),
+        _dptr(xq, torch.uint8, (M, K // 2), "xq"), _dptr(xs, sd, _scale_shape(K, M, precision), "xs"),
+        _dptr(wq, torch.uint8, (N, K // 2), "wq"), _dptr(ws, sd, _scale_shape(K, N, precision), "ws"),
         _dptr(lora_act, torch.float32, (M, rank), "lora_act") if rank else None,
         _dptr(lora_up, torch.bfloat16, (N, rank), "lora_up") if rank else None,
         _dptr(bias, torch.bfloat16, (N,), "bias"),

@@ -118,7 +118,6 @@ int svdq_quantize_act_lora_down(const void* x, int M, int K, const float* smooth
   if (M < 1) return SVDQ_ERR_SHAPE;
   if ((st = check_k(K, precision))) return st;
   if ((st = check_rank(rank, K, K))) return st;
-  if (precision != SVDQ_INT4) return SVDQ_ERR_INVALID_ARG;
   if ((st = current_device_ok())) return st;
   return hip_status(svdq_launch_quantize_act_lora_down(x, M, K, smooth_inv, lora_down, rank, precision, xq, xs,
                                                        lora_act, stream));
@@ -138,7 +137,6 @@ int svdq_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs, const uint8_t* wq,
   if (M < 1 || N < 1) return SVDQ_ERR_SHAPE;
   if ((st = check_k(K, precision))) return st;
   if ((st = check_rank(rank, K, N))) return st;
-  if (precision != SVDQ_INT4) return SVDQ_ERR_INVALID_ARG;
   if ((st = current_device_ok())) return st;
   return hip_status(svdq_launch_gemm_w4a4_lora_up(xq, xs, wq, ws, lora_act, lora_up, bias, y, M, N, K, rank,
                                                   precision, stream));

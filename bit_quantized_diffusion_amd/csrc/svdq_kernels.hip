@@ -92,10 +92,20 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
 
 constexpr int kK1Rows = 64;       // rows per workgroup (4 waves x 16)
 
-template <int RT, bool ATOMIC, bool QUANT = true>
+// Quantizer of kernel 1 (QMODE): kQuantNone = down projection only (the
+// unfused baseline's second kernel), kQuantInt4 = INT4 groups of 64 with fp16
+// scales, kQuantMx = MXFP4 blocks of 32 with E8M0 scales.
+constexpr int kQuantNone = 0, kQuantInt4 = 1, kQuantMx = 2;
+
+// Bits of 2^e as fp32 for e in [-127, 127] (2^-127 is a subnormal).
+__device__ __forceinline__ float exp2i_f32(int e) {
+  return e >= -126 ? __uint_as_float(static_cast<uint32_t>(e + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+template <int RT, bool ATOMIC, int QMODE = kQuantInt4>
 __global__ __launch_bounds__(256) void k1_quant_down_int4(
     const uint16_t* __restrict__ x, int M, int K, const float* __restrict__ sinv,
-    const uint16_t* __restrict__ ldown, uint8_t* __restrict__ xq, uint16_t* __restrict__ xs,
+    const uint16_t* __restrict__ ldown, uint8_t* __restrict__ xq, void* __restrict__ xs_,
     float* __restrict__ lact, int ks) {
   constexpr int RANK = RT * 16;
   constexpr int TB = RT < 2 ? (RT > 0 ? RT : 1) : 2;    // L1 fragments per batch of loads (ranks of 16)
@@ -179,7 +189,8 @@ __global__ __launch_bounds__(256) void k1_quant_down_int4(
       }
     }
 
-    if constexpr (QUANT) {
+    if constexpr (QMODE == kQuantInt4) {
+      uint16_t* xs = static_cast<uint16_t*>(xs_);
       const int g = kbase / 64 + (q >> 1);
       float amax = 0.f;
 #pragma unroll
@@ -207,6 +218,44 @@ __global__ __launch_bounds__(256) void k1_quant_down_int4(
       if (row_ok && valid)
         *reinterpret_cast<uint4*>(xq + xrow / 2 + (kbase + q * 32) / 2) = make_uint4(word[0], word[1], word[2], word[3]);
       if (row_ok && valid && (q & 1) == 0) xs[static_cast<size_t>(g) * M + row] = static_cast<uint16_t>(sbits);
+    } else if constexpr (QMODE == kQuantMx) {
+      // MXFP4 (OCP MX): the lane's 32 k are one block.  e = floor(log2
+      // amax) - 2 from the fp32 exponent field, clamped to [-127, 127];
+      // scale byte e + 127 (amax == 0 gives byte 0 and zero codes).  The
+      // elements x^ / 2^e are rounded to E2M1 by v_cvt_scalef32_pk_fp4_f32
+      // (nearest, ties to the even code, saturating at 6); a value that
+      // rounds to zero keeps no sign.  For the two smallest exponents the
+      // elements are scaled by 2^64 first so that the scale stays normal.
+      uint8_t* xs = static_cast<uint8_t*>(xs_);
+      float amax = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(xh[c][e]));
+      int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFFu) - 127 - 2;
+      e = max(-127, min(127, e));
+      const bool tiny = e < -125;
+      const float pre = tiny ? 18446744073709551616.0f : 1.0f;     // 2^64
+      const float scale = exp2i_f32(tiny ? e + 64 : e);
+      uint32_t word[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        // byte b of the word = codes of k 2b (low nibble) and 2b + 1
+        uint32_t w = 0;
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xh[c][0] * pre, xh[c][1] * pre, scale, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xh[c][2] * pre, xh[c][3] * pre, scale, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xh[c][4] * pre, xh[c][5] * pre, scale, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xh[c][6] * pre, xh[c][7] * pre, scale, 3);
+        // clear the sign of zero magnitudes: bit 3 of a nibble survives
+        // only where its magnitude (bits 0-2) is non-zero
+        const uint32_t mag = w & 0x77777777u;
+        w = mag | (w & ((mag + 0x77777777u) & 0x88888888u));
+        word[c] = w;
+      }
+      if (row_ok && valid) {
+        *reinterpret_cast<uint4*>(xq + xrow / 2 + (kbase + q * 32) / 2) = make_uint4(word[0], word[1], word[2], word[3]);
+        xs[static_cast<size_t>(kbase / 32 + q) * M + row] = static_cast<uint8_t>(e + 127);
+      }
     }
 
     if constexpr (RT > 0) {
@@ -497,6 +546,11 @@ __global__ __launch_bounds__(kK2Threads, 4) void k2_gemm_w4a4(
     const bool more = g + 2 < G;
     if (more) gload(g + 2, ld);
     compute(g, buf_c);
+    // Keep group g's MFMAs and dequant ahead of the wait for group g+2's
+    // loads: the compiler otherwise sinks that pure arithmetic below the
+    // conditional LDS store, and every group then waits out the full
+    // global-memory latency.
+    if constexpr (!DEBUG) asm volatile("" : "+v"(acc[0]), "+v"(acc[1])::"memory");
     if (more) lstore(Slot<(buf + 2) % 3>{}, ld);
     __syncthreads();
   };
@@ -561,10 +615,288 @@ __global__ __launch_bounds__(kK2Threads, 4) void k2_gemm_w4a4(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Kernel 2, MXFP4: FP4 GEMM with E8M0 block scales + up projection + bias.
+//
+// The packed E2M1 nibbles are the matrix core's own FP4 format and the E8M0
+// bytes are its block scales, so v_mfma_scale_f32_32x32x64_f8f6f4 (A and B
+// as FP4) takes both straight from LDS: no conversion and no dequant work.
+// One instruction covers 64 k = two MX blocks: lane half h holds the 32 k of
+// block h of its row (16 bytes) and supplies that block's scale byte.
+//
+// Output tile 128 (n) x 128 (m) per workgroup of 4 waves, 64 x 64 per wave
+// (2 x 2 MFMA tiles, Y^T orientation as in the INT4 kernel).  A pipeline
+// stage is 256 k: 128 code bytes and 8 scale bytes per row (the last stage
+// is a half stage when K % 256 == 128).  Per stage every thread loads four
+// 16-byte chunks of W and four of X (eight lanes cover one 128-byte row
+// segment) and one dword (4 rows of one block) of the W and of the X scales,
+// which stay group-major in LDS ([block][row] bytes).
+//
+// Two-slot LDS ring: at the top of iteration g the registers holding stage
+// g+1 (loaded during iteration g-1) are stored into slot (g+1)%2, the loads
+// of stage g+2 are issued and stage g is computed from slot g%2; one barrier
+// per stage.  A global load so has a whole stage of MFMA work plus the
+// barrier to arrive before anything waits for it.
+//
+// Epilogue: the up projection on the accumulators, the bias, one rounding
+// to bf16; the tile then goes through LDS so that each store writes 16
+// contiguous bytes and eight lanes fill a 128-byte segment of a Y row.
+// ---------------------------------------------------------------------------
+constexpr int kMxStage = 256;                    // k per pipeline stage
+constexpr int kMxStageB = kMxStage / 2;          // code bytes per row and stage
+constexpr int kMxRow = kMxStageB + 16;           // LDS row stride in bytes (16 bytes of padding)
+constexpr int kMxSlot = 2 * kTile * kMxRow;      // one ring slot: W rows, then X rows
+constexpr int kMxThreads = 256;
+constexpr int kMxYRow = kTile + 8;               // staging row stride of the output tile (bf16 elements)
+static_assert(2 * kMxSlot >= kTile * kMxYRow * 2, "output staging fits in the ring");
+
+// One FP4 x FP4 MFMA over 64 k with per-lane block scales (byte 0 of sa, sb).
+__device__ __forceinline__ v16f mfma_fp4(const v4i& a, const v4i& b, const v16f& c, uint32_t sa, uint32_t sb) {
+  const v8i a8 = __builtin_shufflevector(a, v4i{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
+  const v8i b8 = __builtin_shufflevector(b, v4i{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, static_cast<int>(sa), 0,
+                                                         static_cast<int>(sb));
+}
+
+__global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_mxfp4(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+    const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws,
+    const float* __restrict__ lact, const uint16_t* __restrict__ lup,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N, int K, int rank) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_c[2][kMxSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_s[2][2][8][kTile];   // [slot][W|X][block][row]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+  const int wn = wave >> 1, wm = wave & 1;     // 2 x 2 waves: 64 n x 64 m each
+  const int S = (K + kMxStage - 1) / kMxStage;
+  const bool half_last = (K % kMxStage) != 0;  // then K % 256 == 128
+  const size_t kb = static_cast<size_t>(K / 2);
+
+  const TileCoord tc = tile_coord(blockIdx.x, (N + kTile - 1) / kTile, (M + kTile - 1) / kTile);
+  const int n0 = tc.n0, m0 = tc.m0;
+
+  // code loads: rows wave*32 + 8i + lane/8 of W and X, chunk lane%8; rows
+  // past the matrix edge are clamped to its last row (never stored)
+  const int lr = wave * 32 + (lane >> 3), lc = lane & 7;
+  const uint8_t* wsrc[4];
+  const uint8_t* xsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    wsrc[i] = wq + static_cast<size_t>(min(n0 + lr + 8 * i, N - 1)) * kb + lc * 16;
+    xsrc[i] = xq + static_cast<size_t>(min(m0 + lr + 8 * i, M - 1)) * kb + lc * 16;
+  }
+  const int ldst = lr * kMxRow + lc * 16;
+  // scale loads: thread t moves rows 4(t%32) .. +3 of block t/32 of the
+  // stage for W and for X; one dword where the 4 rows are inside the
+  // matrix and aligned, else 4 bytes from rows clamped into the matrix
+  const int sblk = tid >> 5, sr = (tid & 31) * 4;
+  const bool w_dw = (N % 4) == 0 && n0 + sr + 3 < N;
+  const bool x_dw = (M % 4) == 0 && m0 + sr + 3 < M;
+  auto scale4 = [&](const uint8_t* col, int r0, int rows, bool dw) -> uint32_t {
+    if (dw) return *reinterpret_cast<const uint32_t*>(col + r0);
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v |= static_cast<uint32_t>(col[min(r0 + i, rows - 1)]) << (8 * i);
+    return v;
+  };
+
+  struct LoadRegs {
+    uint4 w0, w1, w2, w3, x0, x1, x2, x3;
+    uint32_t s0, s1;
+  };
+  // stage st.  In a half stage the second 64 bytes of a row and the second
+  // scale dword are never read: those lanes re-read bytes inside the row.
+  auto gload = [&](int st) {
+    LoadRegs L;
+    const bool full = (st + 1) * kMxStageB <= static_cast<int>(kb);
+    const int off = st * kMxStageB - (full || lc < 4 ? 0 : kMxStageB / 2);
+    L.w0 = *reinterpret_cast<const uint4*>(wsrc[0] + off);
+    L.w1 = *reinterpret_cast<const uint4*>(wsrc[1] + off);
+    L.w2 = *reinterpret_cast<const uint4*>(wsrc[2] + off);
+    L.w3 = *reinterpret_cast<const uint4*>(wsrc[3] + off);
+    L.x0 = *reinterpret_cast<const uint4*>(xsrc[0] + off);
+    L.x1 = *reinterpret_cast<const uint4*>(xsrc[1] + off);
+    L.x2 = *reinterpret_cast<const uint4*>(xsrc[2] + off);
+    L.x3 = *reinterpret_cast<const uint4*>(xsrc[3] + off);
+    const size_t blk = static_cast<size_t>(8 * st + (full || sblk < 4 ? sblk : sblk - 4));
+    L.s0 = scale4(ws + blk * N, n0 + sr, N, w_dw);
+    L.s1 = scale4(xs + blk * M, m0 + sr, M, x_dw);
+    return L;
+  };
+  auto lstore = [&](auto buf_c, LoadRegs L) {
+    constexpr int buf = decltype(buf_c)::value;
+    uint8_t* wd = &lds_c[buf][0] + ldst;
+    uint8_t* xd = &lds_c[buf][kTile * kMxRow] + ldst;
+    *reinterpret_cast<uint4*>(wd) = L.w0;
+    *reinterpret_cast<uint4*>(wd + 8 * kMxRow) = L.w1;
+    *reinterpret_cast<uint4*>(wd + 16 * kMxRow) = L.w2;
+    *reinterpret_cast<uint4*>(wd + 24 * kMxRow) = L.w3;
+    *reinterpret_cast<uint4*>(xd) = L.x0;
+    *reinterpret_cast<uint4*>(xd + 8 * kMxRow) = L.x1;
+    *reinterpret_cast<uint4*>(xd + 16 * kMxRow) = L.x2;
+    *reinterpret_cast<uint4*>(xd + 24 * kMxRow) = L.x3;
+    *reinterpret_cast<uint32_t*>(&lds_s[buf][0][sblk][sr]) = L.s0;
+    *reinterpret_cast<uint32_t*>(&lds_s[buf][1][sblk][sr]) = L.s1;
+  };
+
+  v16f acc[2][2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it)
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[it][jt][r] = 0.f;
+
+  // 64-k substep s of a stage: code bytes 32s + 16h of the row, which are
+  // block 2s+h of the stage, and that block's scale byte
+  auto compute = [&](auto buf_c, bool half) {
+    constexpr int buf = decltype(buf_c)::value;
+    const uint8_t* wsc = &lds_s[buf][0][h][wn * 64 + l32];
+    const uint8_t* xsc = &lds_s[buf][1][h][wm * 64 + l32];
+    const uint8_t* wb = &lds_c[buf][0] + (wn * 64 + l32) * kMxRow + 16 * h;
+    const uint8_t* xb = &lds_c[buf][kTile * kMxRow] + (wm * 64 + l32) * kMxRow + 16 * h;
+    auto sub = [&](auto s_c) {
+      constexpr int s = decltype(s_c)::value;
+      v4i a[2], b[2];
+      uint32_t sa[2], sb[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        a[t] = *reinterpret_cast<const v4i*>(wb + t * 32 * kMxRow + 32 * s);
+        b[t] = *reinterpret_cast<const v4i*>(xb + t * 32 * kMxRow + 32 * s);
+        sa[t] = wsc[2 * s * kTile + t * 32];
+        sb[t] = xsc[2 * s * kTile + t * 32];
+      }
+#pragma unroll
+      for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+          acc[it][jt] = mfma_fp4(a[it], b[jt], acc[it][jt], sa[it], sb[jt]);
+    };
+    sub(Slot<0>{});
+    sub(Slot<1>{});
+    if (!half) {
+      sub(Slot<2>{});
+      sub(Slot<3>{});
+    }
+  };
+
+  LoadRegs ld = gload(0);
+  lstore(Slot<0>{}, ld);
+  if (S > 1) ld = gload(1);
+  __syncthreads();
+
+  auto iteration = [&](int st, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    if (st + 1 < S) lstore(Slot<1 - buf>{}, ld);
+    if (st + 2 < S) ld = gload(st + 2);
+    compute(buf_c, half_last && st == S - 1);
+    __syncthreads();
+  };
+  for (int st = 0; st < S; st += 2) {
+    iteration(st, Slot<0>{});
+    if (st + 1 < S) iteration(st + 1, Slot<1>{});
+  }
+
+  // up projection: acc += bf16(lora_act) . L2, 16 ranks per MFMA
+  for (int c0 = 0; c0 < rank; c0 += 16) {
+    const int j = c0 + 8 * h;
+    v4i ub[2], ua[2];
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+      const int m = m0 + wm * 64 + jt * 32 + l32;
+      ub[jt] = v4i{0, 0, 0, 0};
+      if (m < M) {
+        const float4* src = reinterpret_cast<const float4*>(lact + static_cast<size_t>(m) * rank + j);
+        const float4 f0 = src[0], f1 = src[1];
+        ub[jt] = v4i{static_cast<int>(pack_bf16_rne(f0.x, f0.y)), static_cast<int>(pack_bf16_rne(f0.z, f0.w)),
+                     static_cast<int>(pack_bf16_rne(f1.x, f1.y)), static_cast<int>(pack_bf16_rne(f1.z, f1.w))};
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int n = n0 + wn * 64 + it * 32 + l32;
+      ua[it] = n < N ? *reinterpret_cast<const v4i*>(lup + static_cast<size_t>(n) * rank + j) : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+        acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ua[it]),
+                                                              __builtin_bit_cast(v8bf, ub[jt]), acc[it][jt], 0, 0, 0);
+  }
+
+  // bias (per channel: 4 consecutive channels per lane and 8-channel group)
+  float bv[2][4][4];
+#pragma unroll
+  for (int it = 0; it < 2; ++it)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int nb = n0 + wn * 64 + it * 32 + 8 * j + 4 * h;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bv[it][j][i] = 0.f;
+      if (bias) {
+        if ((N % 4) == 0 && nb + 3 < N) {
+          const uint2 b2 = *reinterpret_cast<const uint2*>(bias + nb);
+          bv[it][j][0] = __uint_as_float(b2.x << 16);
+          bv[it][j][1] = __uint_as_float(b2.x & 0xFFFF0000u);
+          bv[it][j][2] = __uint_as_float(b2.y << 16);
+          bv[it][j][3] = __uint_as_float(b2.y & 0xFFFF0000u);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (nb + i < N) bv[it][j][i] = __uint_as_float(static_cast<uint32_t>(bias[nb + i]) << 16);
+        }
+      }
+    }
+
+  // Y = bf16(acc + bias), one rounding, into the staging tile [m][n]
+  uint16_t* stg = reinterpret_cast<uint16_t*>(&lds_c[0][0]);
+#pragma unroll
+  for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ml = wm * 64 + jt * 32 + l32;
+        const int nl = wn * 64 + it * 32 + 8 * j + 4 * h;
+        const uint32_t h0 = bf16_rne_bits(acc[it][jt][4 * j + 0] + bv[it][j][0]);
+        const uint32_t h1 = bf16_rne_bits(acc[it][jt][4 * j + 1] + bv[it][j][1]);
+        const uint32_t h2 = bf16_rne_bits(acc[it][jt][4 * j + 2] + bv[it][j][2]);
+        const uint32_t h3 = bf16_rne_bits(acc[it][jt][4 * j + 3] + bv[it][j][3]);
+        *reinterpret_cast<uint2*>(stg + ml * kMxYRow + nl) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+      }
+  __syncthreads();
+
+  // 16-byte stores: thread t writes channels 8(t%16) .. +7 of tile rows t/16 + 16i
+  const int c8 = (tid & 15) * 8;
+  const int n = n0 + c8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = (tid >> 4) + 16 * i;
+    const int m = m0 + r;
+    if (m < M && n < N) {
+      const uint4 v = *reinterpret_cast<const uint4*>(stg + r * kMxYRow + c8);
+      uint16_t* dst = y + static_cast<size_t>(m) * N + n;
+      if ((N % 8) == 0) {
+        *reinterpret_cast<uint4*>(dst) = v;
+      } else {
+        const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (n + e < N) dst[e] = static_cast<uint16_t>(vv[e / 2] >> (16 * (e % 2)));
+      }
+    }
+  }
+}
+
 // K1 grid: 64-row blocks x K slices.  The slice count is chosen so that
 // the grid holds about four workgroups per CU (256 CUs), with slices of
 // whole 128-k steps.
-template <int RT, bool QUANT = true>
+template <int RT, int QMODE = kQuantInt4>
 hipError_t launch_k1(const void* x, int M, int K, const float* sinv, const void* ldown, uint8_t* xq, void* xs,
                      float* lact, hipStream_t st) {
   const int row_blocks = (M + kK1Rows - 1) / kK1Rows;
@@ -581,11 +913,11 @@ hipError_t launch_k1(const void* x, int M, int K, const float* sinv, const void*
   if (atomic) {
     const size_t n = static_cast<size_t>(M) * RT * 16;
     hipLaunchKernelGGL(fill_zero_f32, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, lact, n);
-    hipLaunchKernelGGL((k1_quant_down_int4<RT, true, QUANT>), grid, block, lds, st, static_cast<const uint16_t*>(x), M, K,
-                       sinv, static_cast<const uint16_t*>(ldown), xq, static_cast<uint16_t*>(xs), lact, ks);
+    hipLaunchKernelGGL((k1_quant_down_int4<RT, true, QMODE>), grid, block, lds, st, static_cast<const uint16_t*>(x), M, K,
+                       sinv, static_cast<const uint16_t*>(ldown), xq, xs, lact, ks);
   } else {
-    hipLaunchKernelGGL((k1_quant_down_int4<RT, false, QUANT>), grid, block, lds, st, static_cast<const uint16_t*>(x), M, K,
-                       sinv, static_cast<const uint16_t*>(ldown), xq, static_cast<uint16_t*>(xs), lact, ks);
+    hipLaunchKernelGGL((k1_quant_down_int4<RT, false, QMODE>), grid, block, lds, st, static_cast<const uint16_t*>(x), M, K,
+                       sinv, static_cast<const uint16_t*>(ldown), xq, xs, lact, ks);
   }
   return hipGetLastError();
 }
@@ -670,7 +1002,7 @@ hipError_t launch_unfused(const void* x, int M, int K, const float* sinv, const 
   hipError_t e = launch_k1<0>(x, M, K, sinv, nullptr, xq, xs, nullptr, st);           // 1: quantize
   if (e != hipSuccess) return e;
   if constexpr (RT > 0) {
-    e = launch_k1<RT, false>(x, M, K, sinv, ldown, xq, xs, lact, st);                 // 2: down projection
+    e = launch_k1<RT, kQuantNone>(x, M, K, sinv, ldown, xq, xs, lact, st);            // 2: down projection
     if (e != hipSuccess) return e;
   }
   const int tiles = ((N + kTile - 1) / kTile) * ((M + kTile - 1) / kTile);               // 3: 4-bit GEMM
@@ -689,13 +1021,15 @@ hipError_t launch_unfused(const void* x, int M, int K, const float* sinv, const 
 extern "C" int svdq_launch_quantize_act_lora_down(const void* x, int M, int K, const float* smooth_inv,
                                                   const void* lora_down, int rank, int precision, uint8_t* xq,
                                                   void* xs, float* lora_act, void* stream) {
-  if (precision != SVDQ_INT4) return static_cast<int>(hipErrorInvalidValue);
+  if (precision != SVDQ_INT4 && precision != SVDQ_MXFP4) return static_cast<int>(hipErrorInvalidValue);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool mx = precision == SVDQ_MXFP4;
   hipError_t e;
   switch (rank / 16) {
-#define SVDQ_K1_CASE(R) \
-  case R:               \
-    e = launch_k1<R>(x, M, K, smooth_inv, lora_down, xq, xs, lora_act, st); \
+#define SVDQ_K1_CASE(R)                                                                        \
+  case R:                                                                                      \
+    e = mx ? launch_k1<R, kQuantMx>(x, M, K, smooth_inv, lora_down, xq, xs, lora_act, st)      \
+           : launch_k1<R, kQuantInt4>(x, M, K, smooth_inv, lora_down, xq, xs, lora_act, st); \
     break;
     SVDQ_K1_CASE(0) SVDQ_K1_CASE(1) SVDQ_K1_CASE(2) SVDQ_K1_CASE(3) SVDQ_K1_CASE(4) SVDQ_K1_CASE(5)
     SVDQ_K1_CASE(6) SVDQ_K1_CASE(7) SVDQ_K1_CASE(8) SVDQ_K1_CASE(9) SVDQ_K1_CASE(10) SVDQ_K1_CASE(11)
@@ -710,8 +1044,15 @@ extern "C" int svdq_launch_quantize_act_lora_down(const void* x, int M, int K, c
 extern "C" int svdq_launch_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs, const uint8_t* wq, const void* ws,
                                              const float* lora_act, const void* lora_up, const void* bias, void* y,
                                              int M, int N, int K, int rank, int precision, void* stream) {
-  if (precision != SVDQ_INT4) return static_cast<int>(hipErrorInvalidValue);
+  if (precision != SVDQ_INT4 && precision != SVDQ_MXFP4) return static_cast<int>(hipErrorInvalidValue);
   const int tiles = ((N + kTile - 1) / kTile) * ((M + kTile - 1) / kTile);
+  if (precision == SVDQ_MXFP4) {
+    hipLaunchKernelGGL(k2_gemm_mxfp4, dim3(tiles), dim3(kMxThreads), 0, static_cast<hipStream_t>(stream), xq,
+                       static_cast<const uint8_t*>(xs), wq, static_cast<const uint8_t*>(ws), lora_act,
+                       static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias),
+                       static_cast<uint16_t*>(y), M, N, K, rank);
+    return static_cast<int>(hipGetLastError());
+  }
   hipLaunchKernelGGL(k2_gemm_w4a4<false>, dim3(tiles), dim3(kK2Threads), 0, static_cast<hipStream_t>(stream), xq,
                      static_cast<const uint16_t*>(xs), wq, static_cast<const uint16_t*>(ws), lora_act,
                      static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias),

@@ -135,7 +135,13 @@ SVDQ_API int svdq_pack_weights(const uint16_t* w_bf16, const float* act_absmax,
  * X^ = bf16(fp32(x * smooth_inv)) is rounded once and feeds both branches.
  * INT4 rule per 64-group of a row: s = fp16(fp32(amax/7)) (round to
  * nearest even, saturating at 65504), s == 0 -> codes 0, else
- * q = clamp(rint(fp32(x^ * fp32(1/s))), -7, 7), ties to even. */
+ * q = clamp(rint(fp32(x^ * fp32(1/s))), -7, 7), ties to even.
+ * MXFP4 rule per 32-block (OCP Microscaling v1.0): amax == 0 -> byte 0 and
+ * codes 0; else e = clamp(floor(log2 amax) - 2, -127, 127) from the fp32
+ * exponent field, byte e + 127, code = E2M1(x^ / 2^e) rounded to nearest
+ * (ties to the even code, saturating at 6); zero magnitudes carry no sign.
+ * lora_act partials of several workgroups may be summed with fp32 atomics,
+ * so its last bits can differ between calls. */
 SVDQ_API int svdq_quantize_act_lora_down(const void* x, int M, int K,
                                 const float* smooth_inv, const void* lora_down,
                                 int rank, int precision,
@@ -154,7 +160,9 @@ SVDQ_API int svdq_quantize_act_lora_down(const void* x, int M, int K,
  * INT4: for every 64-group g the exact integer partial
  * P = sum_k qx qw is scaled by s_x[m,g] s_w[n,g] into fp32 accumulators;
  * the up projection bf16(lora_act) L2 and the bias are added in fp32 and Y
- * is rounded to bf16 once. */
+ * is rounded to bf16 once.  MXFP4: the E2M1 codes with their E8M0 block
+ * scales go to the matrix core as they are (fp32 accumulation); up
+ * projection, bias and rounding as for INT4. */
 SVDQ_API int svdq_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs,
                            const uint8_t* wq, const void* ws,
                            const float* lora_act, const void* lora_up,

@@ -69,3 +69,20 @@ def mlp_pair():
     pk2.pop("w_hat", None)
     fc2 = dict(spec=spec2, x=x2, w=w2, bias=b2, ax=ax2, pk=pk2, rank=spec2.rank)
     return fc1, fc2
+
+
+def mx_pack(case):
+    """MXFP4 weights of a case: the same smoothing and SVD branch, the
+    residual quantized in MXFP4 by the oracle."""
+    return O.mx_pack_weights(None, None, case["rank"], svd_cache=case["pk"])
+
+
+def mx_oracle_rows(case, rows, x_bits=None):
+    """MXFP4 oracle of the whole layer on a subset of token rows."""
+    x = case["x"] if x_bits is None else x_bits
+    pk = mx_pack(case)
+    sub = np.ascontiguousarray(x[rows])
+    a = O.mx_quantize_act_lora_down(sub, pk["smooth_inv"], pk["l1"])
+    b = O.mx_gemm_lora_up(a["xq"], a["xs"], pk["wq"], pk["ws"], a["t"], pk["l2"], case["bias"])
+    b.update(a)
+    return b
