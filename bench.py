@@ -18,6 +18,10 @@ ops (2*M*N*K, the same for fc1 and fc2) over its average launch time,
 timed with HIP events on the stream the library launches on, against the
 dense 8-bit matrix-core peak (int8 and fp8 run at the same rate).
 
+The `mxfp4` object times the same two layers packed in MXFP4 (E2M1 codes,
+E8M0 scales per 32 k) outside the timed step, against the dense FP4
+matrix-core peak.
+
 `--calibrate-copy` instead runs a plain elementwise copy of 1 GiB a few
 times; its FETCH_SIZE / WRITE_SIZE counters give the factor that turns the
 counters read on the GEMM into HBM bytes.
@@ -37,11 +41,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = ("fused W4A4+LoRA-r32 linear: µs/layer, TOPS & % INT8-MFMA roofline (FLUX MLP)")
 INT8_PEAK_TOPS = 5033.0        # 256 CU x 2.4 GHz x 8192 int8/fp8 ops/clk/CU (dense)
+FP4_PEAK_TOPS = 10066.0        # 256 CU x 2.4 GHz x 16384 fp4 ops/clk/CU (dense)
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "bit_quantized_diffusion_amd", "csrc", "svdq_kernels.hip")
-TRAFFIC = os.path.join(ROOT, "profiles", "k2_gemm_w4a4_flux_mlp_hbm_traffic.md")
+TRAFFIC = os.path.join(ROOT, "profiles", "k2_gemm_int4_flux_mlp_hbm_traffic.md")
 TRAFFIC_NOTE = ("rocprofv3 FETCH_SIZE + WRITE_SIZE per launch, scaled by the elementwise-copy "
-                "calibration (profiles/k2_gemm_w4a4_flux_mlp_hbm_traffic.md)")
+                "calibration (profiles/k2_gemm_int4_flux_mlp_hbm_traffic.md)")
 
 
 def log(*a):
@@ -62,6 +67,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-ablation", action="store_true",
                    help="skip the fused-vs-unfused (four kernel) comparison")
+    p.add_argument("--no-mxfp4", action="store_true", help="skip the MXFP4 timing of the same layers")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="time budget of the oracle sample (whole chunks of rows)")
     p.add_argument("--cpu-chunk", type=int, default=96, help="token rows per oracle chunk")
@@ -224,7 +230,7 @@ def main():
     traffic, traffic_state = read_traffic()
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic,
-                "kernel": "k2_gemm_w4a4 (fc1 4608x3072->12288 and fc2 4608x12288->3072)",
+                "kernel": "k2_gemm_int4 (fc1 4608x3072->12288 and fc2 4608x12288->3072)",
                 "avg_launch_us": round(k2_us, 2), "ops_per_launch": k2_ops,
                 "peak_basis": "dense int8/fp8 matrix-core rate, 256 CU x 2.4 GHz x 8192 ops/clk",
                 "traffic_source": TRAFFIC_NOTE if traffic is not None else
@@ -233,6 +239,11 @@ def main():
     ablation = None
     if not args.no_ablation:
         ablation = fusion_ablation(bq, torch, np, sets, M, (s1, s2), per, stream, reps=10)
+
+    mx = None
+    if not args.no_mxfp4:
+        mx = mxfp4_layers(bq, torch, np, dev, (s1, s2), (lay1["w"], w2), (ax1, ax2),
+                          (lay1["bias"], synth.gen_bias(s2)), (x1, x2), args.sets, stream, reps=20)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -250,6 +261,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "fusion_ablation": ablation,
+        "mxfp4": mx,
     }
     print(json.dumps(out), flush=True)
 
@@ -296,6 +308,63 @@ def fusion_ablation(bq, torch, np, sets, M, specs, per, stream, reps):
                     "algorithmic_mb_unfused": round(unfused_b / 1e6, 1),
                     "mb_saved_by_fusion": round((unfused_b - fused_b) / 1e6, 1)}
     log(f"bench: fusion ablation {json.dumps(out)}")
+    return out
+
+
+def mxfp4_layers(bq, torch, np, dev, specs, ws, axs, biases, xs, n_sets, stream, reps):
+    """The same fc1 / fc2 layers (same weights, activations and bias) packed
+    in MXFP4; both kernels timed per launch with HIP events on the library's
+    stream, over rotated buffer sets, outside the timed step."""
+    out = {}
+    k2_all = []
+    for tag, s, w, ax, bias, x in zip(("fc1", "fc2"), specs, ws, axs, biases, xs):
+        pk = bq.pack_weights(w, ax, s.rank, precision=bq.MXFP4)
+        L = bq.PackedLinear.from_host(pk, bias, s.rank, precision=bq.MXFP4, device=dev)
+        sets = []
+        for _ in range(n_sets):
+            sets.append(dict(x=x.clone(), wq=L.wq.clone(), ws=L.ws.clone(),
+                             xq=torch.empty((s.M, s.K // 2), dtype=torch.uint8, device=dev),
+                             xs=torch.empty((s.K // 32, s.M), dtype=torch.uint8, device=dev),
+                             la=torch.empty((s.M, s.rank), dtype=torch.float32, device=dev),
+                             y=torch.empty((s.M, s.N), dtype=torch.bfloat16, device=dev)))
+
+        def run(b, record, evs):
+            if record:
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                e[0].record(stream)
+            bq.quantize_act_lora_down(b["x"], L.smooth_inv, L.lora_down, s.rank, bq.MXFP4, xq=b["xq"], xs=b["xs"],
+                                      lora_act=b["la"])
+            if record:
+                e[1].record(stream)
+            bq.gemm_w4a4_lora_up(b["xq"], b["xs"], b["wq"], b["ws"], b["la"], L.lora_up, L.bias, s.M, s.N, s.K,
+                                 s.rank, bq.MXFP4, y=b["y"])
+            if record:
+                e[2].record(stream)
+                evs.append(e)
+
+        for i in range(3):
+            run(sets[i % n_sets], False, None)
+        torch.cuda.synchronize()
+        evs = []
+        for i in range(reps):
+            run(sets[i % n_sets], True, evs)
+        torch.cuda.synchronize()
+        k1 = 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        k2 = 1e3 * float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        k2_all += [e[1].elapsed_time(e[2]) for e in evs]
+        ops = 2.0 * s.M * s.N * s.K
+        out[tag] = {"us_k1": round(k1, 2), "us_k2": round(k2, 2), "us_layer": round(k1 + k2, 2),
+                    "tops": round(ops / ((k1 + k2) * 1e-6) / 1e12, 1),
+                    "pct_fp4_roofline": round(100 * ops / ((k1 + k2) * 1e-6) / 1e12 / FP4_PEAK_TOPS, 2)}
+        del sets
+    k2_us = 1e3 * float(np.mean(k2_all))
+    ops = 2.0 * specs[0].M * specs[0].N * specs[0].K
+    achieved = ops / (k2_us * 1e-6) / 1e12
+    out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP4_PEAK_TOPS, "unit": "TFLOP/s",
+                       "frac": round(achieved / FP4_PEAK_TOPS, 4), "kernel": "k2_gemm_mxfp4 (fc1 and fc2)",
+                       "avg_launch_us": round(k2_us, 2),
+                       "peak_basis": "dense fp4 matrix-core rate, 256 CU x 2.4 GHz x 16384 ops/clk"}
+    log(f"bench: mxfp4 {json.dumps(out)}")
     return out
 
 

@@ -300,38 +300,23 @@ __global__ void fill_zero_f32(float* __restrict__ p, size_t n) {
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 2: INT4 GEMM + per-group dequant + up projection + bias.
+// Kernel 2 (both precisions): 4-bit GEMM + dequant + up projection + bias.
 //
-// Output tile 128 (n) x 128 (m) per workgroup of 8 waves; each wave owns a
-// 64 (n) x 32 (m) sub-tile = 2 MFMA tiles of 32 x 32.  The MFMA computes Y^T
-// tiles (A = W codes, B = X codes), so a lane ends up with groups of 4
-// consecutive output channels of one token and stores each as one 8-byte
-// write.  The register budget is 128 VGPRs: two workgroups (16 waves) share
-// a CU and hide memory latency.
+// Output tile 128 (n) x 128 (m) per workgroup of 4 waves, 64 x 64 per wave
+// (2 x 2 MFMA tiles of 32 x 32).  The MFMA computes Y^T tiles (A = W codes,
+// B = X codes), so a lane ends up with groups of 4 consecutive output
+// channels of one token; the epilogue turns the tile around in LDS so that
+// Y is written in 16-byte row segments.
 //
-// The 4-bit codes reach the matrix core as FP8 E4M3 subnormals: a
-// sign-magnitude nibble s|mmm becomes the byte s000_0mmm, which is exactly
-// +-m * 2^-9, with four bit operations per 8 codes.  For one K-group of 64,
-// v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales) then returns P * 2^-18 in
-// fp32, exactly: every product is a multiple of 2^-18 and every partial sum
-// stays below 2^24 of those units.  So the group's integer partial P arrives
-// already as a float and the per-group dequant is one multiply (the scale
-// product s_w s_x) and one fma per output element; on gfx950 that VALU work,
-// not the MFMA, bounds the kernel.
-//
-// Per K-group: every thread loads 16 packed bytes of one operand tile from
-// global memory one group ahead (rows past the matrix edge are clamped to
-// the last row; their outputs are never stored), converts them to FP8 and
-// stores them into a three-slot LDS ring (iteration g reads slot g%3 while
-// g+2 is stored into slot (g+2)%3, whose last readers passed the previous
-// barrier; one barrier per group).  After the K loop the 2^18 is applied,
-// the bf16 up projection runs on the same accumulators (MFMA srcC), the bias
-// is added and Y is rounded to bf16 and stored once.
+// INT4 codes reach the matrix core as FP8 E4M3 subnormals: a sign-magnitude
+// nibble s|mmm becomes the byte s000_0mmm, which is exactly +-m * 2^-9.  For
+// one K-group of 64, v_mfma_scale_f32_32x32x64_f8f6f4 then returns the
+// group's integer partial P times 2^-18 times its two E8M0 block scales,
+// exactly: every product is a multiple of 2^-18 and every partial sum stays
+// below 2^24 of those units.  MXFP4 codes are the matrix core's own FP4.
 // ---------------------------------------------------------------------------
 
 constexpr int kTile = 128;      // output tile edge (both n and m)
-constexpr int kLdsRow = 80;     // 64 bytes of FP8 codes + 16 bytes padding
-constexpr int kK2Threads = 512;
 constexpr unsigned kUnitScales = 0x7F7F7F7Fu;   // E8M0 127 = 1.0 in every byte
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -383,238 +368,6 @@ __device__ __forceinline__ void unpack_store_fp8(int8_t* dst, const uint4& w) {
   d[1] = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-template <bool DEBUG>
-__global__ __launch_bounds__(kK2Threads, 4) void k2_gemm_w4a4(
-    const uint8_t* __restrict__ xq, const uint16_t* __restrict__ xs,
-    const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
-    const float* __restrict__ lact, const uint16_t* __restrict__ lup,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
-    int M, int N, int K, int rank,
-    int win_m0, int win_n0, int win_mt, int win_nt, int32_t* __restrict__ dbg) {
-  __shared__ __attribute__((aligned(16))) int8_t lds_w[3][kTile * kLdsRow];
-  __shared__ __attribute__((aligned(16))) int8_t lds_x[3][kTile * kLdsRow];
-  // per group and row: E8M0 exponent byte of the scale (as a dword) and
-  // the fp16 significand in [1, 2); index 0 = W rows, 1 = X rows
-  __shared__ __attribute__((aligned(16))) uint32_t lds_se[DEBUG ? 1 : 3][2][kTile];
-  __shared__ __attribute__((aligned(16))) _Float16 lds_sm[DEBUG ? 1 : 3][2][kTile];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  // wave-uniform, so that the per-wave roles below live in scalar registers
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31;
-  const int h = lane >> 5;
-  const int wn = wave >> 2, wm = wave & 3;     // 2 x 4 waves: 64 n x 32 m each
-  const int G = K / 64;
-  const size_t rowb = static_cast<size_t>(K / 2);
-
-  int n0, m0;
-  if constexpr (DEBUG) {
-    const int tiles_m = (win_mt + kTile - 1) / kTile;
-    n0 = win_n0 + (blockIdx.x / tiles_m) * kTile;
-    m0 = win_m0 + (blockIdx.x % tiles_m) * kTile;
-  } else {
-    const TileCoord tc = tile_coord(blockIdx.x, (N + kTile - 1) / kTile, (M + kTile - 1) / kTile);
-    n0 = tc.n0;
-    m0 = tc.m0;
-  }
-
-  // loader role: threads 0..255 move 16 packed bytes of W row t/2 (half
-  // t%2), threads 256..511 the same for X; rows clamped into the matrix
-  const bool ld_is_w = wave < 4;
-  const int lt = tid & 255;
-  const int lrow = lt >> 1, lhalf = lt & 1;
-  const int src_row = ld_is_w ? min(n0 + lrow, N - 1) : min(m0 + lrow, M - 1);
-  const uint8_t* ldsrc = (ld_is_w ? wq : xq) + static_cast<size_t>(src_row) * rowb + lhalf * 16;
-  int8_t* const lddst0 = (ld_is_w ? &lds_w[0][0] : &lds_x[0][0]) + lrow * kLdsRow + lhalf * 32;
-  // scale role: threads 0..127 move s_w of row n0+t, 128..255 s_x of m0+t-128
-  const bool sc_thread = !DEBUG && wave < 4;
-  const bool sc_is_w = wave < 2;
-  const int sc_i = tid & (kTile - 1);
-  const int sc_row = sc_is_w ? min(n0 + sc_i, N - 1) : min(m0 + sc_i, M - 1);
-  const uint16_t* scsrc = DEBUG ? nullptr : ((sc_is_w ? ws : xs) + sc_row);
-  const size_t sc_stride = sc_is_w ? static_cast<size_t>(N) : static_cast<size_t>(M);
-
-  struct LoadRegs {
-    uint4 c;
-    uint32_t sc;
-  };
-  auto gload = [&](int g, LoadRegs& L) {
-    L.c = *reinterpret_cast<const uint4*>(ldsrc + g * 32);
-    if constexpr (!DEBUG) {
-      if (sc_thread) L.sc = scsrc[static_cast<size_t>(g) * sc_stride];
-    }
-  };
-  // store one group into ring slot BUF.  A scale s (fp16, >= 0) is split
-  // into its binary exponent, which the matrix core applies exactly as an
-  // E8M0 block scale, and its significand in [1, 2), an exact fp16.  Taken
-  // from the fp32 image of s (normal for every fp16 value): the exponent
-  // byte is the fp32 exponent field.  W rows carry an extra 2^18 that
-  // cancels the 2^-18 of the FP8 code encoding.  s == 0 gives byte 0
-  // (2^-127) with significand 1; its codes are all 0, so its products are 0.
-  auto lstore = [&](auto buf_c, const LoadRegs& L) {
-    constexpr int buf = decltype(buf_c)::value;
-    unpack_store_fp8(lddst0 + buf * (kTile * kLdsRow), L.c);
-    if constexpr (!DEBUG) {
-      if (sc_thread) {
-        const uint32_t u = __float_as_uint(f16_bits_to_f32(L.sc));
-        const uint32_t ebyte = ((u >> 23) & 0xFFu) + (sc_is_w && u != 0 ? 18u : 0u);
-        lds_se[buf][sc_is_w ? 0 : 1][sc_i] = ebyte;
-        lds_sm[buf][sc_is_w ? 0 : 1][sc_i] =
-            static_cast<_Float16>(__uint_as_float((u & 0x007FFFFFu) | 0x3F800000u));
-      }
-    }
-  };
-
-  v16f acc[2];
-#pragma unroll
-  for (int it = 0; it < 2; ++it)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[it][r] = 0.f;
-
-  // Per group and 32x32 tile the MFMA returns P * 2^(e_w + e_x) (exact:
-  // the E8M0 scales are powers of two and every value stays a normal fp32);
-  // the significands multiply in packed fp16 (m_w m_x in [1, 4), one
-  // rounding, relative error <= 2^-11) and v_fma_mix_f32 adds P' * (m_w m_x)
-  // into the fp32 accumulator: 1.5 VALU operations per output and group.
-  auto compute = [&](int g, auto buf_c) {
-    constexpr int buf = decltype(buf_c)::value;
-    const int8_t* xrow = &lds_x[buf][(wm * 32 + l32) * kLdsRow + 32 * h];
-    const v8i b = __builtin_shufflevector(*reinterpret_cast<const v4i*>(xrow),
-                                          *reinterpret_cast<const v4i*>(xrow + 16), 0, 1, 2, 3, 4, 5, 6, 7);
-    uint32_t eb = 127u;
-    h2 mx2 = h2{static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
-    if constexpr (!DEBUG) {
-      eb = lds_se[buf][1][wm * 32 + l32];
-      const _Float16 mx = lds_sm[buf][1][wm * 32 + l32];
-      mx2 = h2{mx, mx};
-    }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int8_t* wrow = &lds_w[buf][(wn * 64 + it * 32 + l32) * kLdsRow + 32 * h];
-      const v8i a = __builtin_shufflevector(*reinterpret_cast<const v4i*>(wrow),
-                                            *reinterpret_cast<const v4i*>(wrow + 16), 0, 1, 2, 3, 4, 5, 6, 7);
-      if constexpr (DEBUG) {
-        const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, v16f{}, 0, 0, 0, kUnitScales, 0,
-                                                                       kUnitScales);
-        const int m = m0 + wm * 32 + l32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int n = n0 + wn * 64 + it * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-          if (m < win_m0 + win_mt && n < win_n0 + win_nt)
-            dbg[(static_cast<size_t>(m - win_m0) * win_nt + (n - win_n0)) * G + g] =
-                static_cast<int32_t>(p[r] * 262144.0f);     // exact: P * 2^-18 * 2^18
-        }
-      } else {
-        const uint32_t ea = lds_se[buf][0][wn * 64 + it * 32 + l32];
-        const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, v16f{}, 0, 0, 0, ea, 0, eb);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // significands of the 4 consecutive W rows this lane's elements 4j..4j+3 belong to
-          const uint2 mw = *reinterpret_cast<const uint2*>(&lds_sm[buf][0][wn * 64 + it * 32 + 8 * j + 4 * h]);
-          const h2 s01 = __builtin_bit_cast(h2, mw.x) * mx2;
-          const h2 s23 = __builtin_bit_cast(h2, mw.y) * mx2;
-          acc[it][4 * j + 0] = __builtin_fmaf(p[4 * j + 0], static_cast<float>(s01[0]), acc[it][4 * j + 0]);
-          acc[it][4 * j + 1] = __builtin_fmaf(p[4 * j + 1], static_cast<float>(s01[1]), acc[it][4 * j + 1]);
-          acc[it][4 * j + 2] = __builtin_fmaf(p[4 * j + 2], static_cast<float>(s23[0]), acc[it][4 * j + 2]);
-          acc[it][4 * j + 3] = __builtin_fmaf(p[4 * j + 3], static_cast<float>(s23[1]), acc[it][4 * j + 3]);
-        }
-      }
-      // one tile's products in flight at a time (register budget)
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // prologue: groups 0 and 1 into LDS
-  LoadRegs ld;
-  ld.c = make_uint4(0, 0, 0, 0);
-  ld.sc = 0;
-  gload(0, ld);
-  lstore(Slot<0>{}, ld);
-  if (G > 1) {
-    gload(1, ld);
-    lstore(Slot<1>{}, ld);
-  }
-  __syncthreads();
-
-  // iteration g: issue the loads of g+2, compute g from ring slot g%3,
-  // store g+2 into slot (g+2)%3, barrier.  Unrolled by the ring size so
-  // that every slot address is a compile-time offset.  Waves of the other
-  // workgroup on the CU run while this one waits for its loads.
-  auto iteration = [&](int g, auto buf_c) {
-    constexpr int buf = decltype(buf_c)::value;
-    const bool more = g + 2 < G;
-    if (more) gload(g + 2, ld);
-    compute(g, buf_c);
-    // Keep group g's MFMAs and dequant ahead of the wait for group g+2's
-    // loads: the compiler otherwise sinks that pure arithmetic below the
-    // conditional LDS store, and every group then waits out the full
-    // global-memory latency.
-    if constexpr (!DEBUG) asm volatile("" : "+v"(acc[0]), "+v"(acc[1])::"memory");
-    if (more) lstore(Slot<(buf + 2) % 3>{}, ld);
-    __syncthreads();
-  };
-  for (int g = 0; g < G; g += 3) {
-    iteration(g, Slot<0>{});
-    if (g + 1 < G) iteration(g + 1, Slot<1>{});
-    if (g + 2 < G) iteration(g + 2, Slot<2>{});
-  }
-
-  if constexpr (!DEBUG) {
-    // up projection: acc += bf16(lora_act) . L2 on the same tiles, K = 16
-    // per v_mfma_f32_32x32x16_bf16 (rank is a multiple of 16)
-    const int m = m0 + wm * 32 + l32;
-    for (int c0 = 0; c0 < rank; c0 += 16) {
-      const int j = c0 + 8 * h;          // this lane's 8 k-slots
-      v4i ub = v4i{0, 0, 0, 0};
-      if (m < M) {
-        const float4* src = reinterpret_cast<const float4*>(lact + static_cast<size_t>(m) * rank + j);
-        const float4 f0 = src[0], f1 = src[1];
-        ub = v4i{static_cast<int>(pack_bf16_rne(f0.x, f0.y)), static_cast<int>(pack_bf16_rne(f0.z, f0.w)),
-                 static_cast<int>(pack_bf16_rne(f1.x, f1.y)), static_cast<int>(pack_bf16_rne(f1.z, f1.w))};
-      }
-#pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const int n = n0 + wn * 64 + it * 32 + l32;
-        const v4i ua = n < N ? *reinterpret_cast<const v4i*>(lup + static_cast<size_t>(n) * rank + j)
-                             : v4i{0, 0, 0, 0};
-        acc[it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ua), __builtin_bit_cast(v8bf, ub),
-                                                         acc[it], 0, 0, 0);
-      }
-    }
-
-    if (m < M) {
-      const bool vec_ok = (N % 4) == 0;
-#pragma unroll
-      for (int it = 0; it < 2; ++it) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int nb = n0 + wn * 64 + it * 32 + 8 * j + 4 * h;    // 4 consecutive channels
-          float bv[4] = {0.f, 0.f, 0.f, 0.f};
-          if (bias) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (nb + i < N) bv[i] = __uint_as_float(static_cast<uint32_t>(bias[nb + i]) << 16);
-          }
-          uint16_t* dst = y + static_cast<size_t>(m) * N + nb;
-          const uint32_t h0 = bf16_rne_bits(acc[it][4 * j + 0] + bv[0]);
-          const uint32_t h1 = bf16_rne_bits(acc[it][4 * j + 1] + bv[1]);
-          const uint32_t h2 = bf16_rne_bits(acc[it][4 * j + 2] + bv[2]);
-          const uint32_t h3 = bf16_rne_bits(acc[it][4 * j + 3] + bv[3]);
-          if (vec_ok && nb + 3 < N) {
-            *reinterpret_cast<uint2*>(dst) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-          } else {
-            const uint32_t hs[4] = {h0, h1, h2, h3};
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (nb + i < N) dst[i] = static_cast<uint16_t>(hs[i]);
-          }
-        }
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Kernel 2, MXFP4: FP4 GEMM with E8M0 block scales + up projection + bias.
 //
@@ -649,6 +402,107 @@ constexpr int kMxSlot = 2 * kTile * kMxRow;      // one ring slot: W rows, then 
 constexpr int kMxThreads = 256;
 constexpr int kMxYRow = kTile + 8;               // staging row stride of the output tile (bf16 elements)
 static_assert(2 * kMxSlot >= kTile * kMxYRow * 2, "output staging fits in the ring");
+
+// Shared epilogue of the 128 x 128 GEMM tiles (4 waves of 64 x 64, Y^T
+// MFMA layout): acc += bf16(lora_act) . L2 on the accumulators (16 ranks per
+// v_mfma_f32_32x32x16_bf16), the bias, one rounding to bf16, then the tile
+// goes through LDS (stg: kTile rows of kMxYRow bf16) so that each store
+// writes 16 contiguous bytes and eight lanes fill a 128-byte segment of a Y
+// row.  Every wave must be past its last LDS read of the main loop.
+__device__ __forceinline__ void epilogue_tile128(v16f (&acc)[2][2], uint16_t* __restrict__ stg,
+                                                 const float* __restrict__ lact, const uint16_t* __restrict__ lup,
+                                                 const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M,
+                                                 int N, int rank, int n0, int m0, int wn, int wm, int l32, int h,
+                                                 int tid) {
+  for (int c0 = 0; c0 < rank; c0 += 16) {
+    const int j = c0 + 8 * h;
+    v4i ub[2], ua[2];
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+      const int m = m0 + wm * 64 + jt * 32 + l32;
+      ub[jt] = v4i{0, 0, 0, 0};
+      if (m < M) {
+        const float4* src = reinterpret_cast<const float4*>(lact + static_cast<size_t>(m) * rank + j);
+        const float4 f0 = src[0], f1 = src[1];
+        ub[jt] = v4i{static_cast<int>(pack_bf16_rne(f0.x, f0.y)), static_cast<int>(pack_bf16_rne(f0.z, f0.w)),
+                     static_cast<int>(pack_bf16_rne(f1.x, f1.y)), static_cast<int>(pack_bf16_rne(f1.z, f1.w))};
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int n = n0 + wn * 64 + it * 32 + l32;
+      ua[it] = n < N ? *reinterpret_cast<const v4i*>(lup + static_cast<size_t>(n) * rank + j) : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+        acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ua[it]),
+                                                              __builtin_bit_cast(v8bf, ub[jt]), acc[it][jt], 0, 0, 0);
+  }
+
+  // bias: lane element 4j+i of tile it is channel n0 + wn*64 + it*32 + 8j + 4h + i
+  float bv[2][4][4];
+#pragma unroll
+  for (int it = 0; it < 2; ++it)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int nb = n0 + wn * 64 + it * 32 + 8 * j + 4 * h;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bv[it][j][i] = 0.f;
+      if (bias) {
+        if ((N % 4) == 0 && nb + 3 < N) {
+          const uint2 b2 = *reinterpret_cast<const uint2*>(bias + nb);
+          bv[it][j][0] = __uint_as_float(b2.x << 16);
+          bv[it][j][1] = __uint_as_float(b2.x & 0xFFFF0000u);
+          bv[it][j][2] = __uint_as_float(b2.y << 16);
+          bv[it][j][3] = __uint_as_float(b2.y & 0xFFFF0000u);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (nb + i < N) bv[it][j][i] = __uint_as_float(static_cast<uint32_t>(bias[nb + i]) << 16);
+        }
+      }
+    }
+
+  // Y = bf16(acc + bias), one rounding, into the staging tile [m][n]
+#pragma unroll
+  for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ml = wm * 64 + jt * 32 + l32;
+        const int nl = wn * 64 + it * 32 + 8 * j + 4 * h;
+        const uint32_t h0 = bf16_rne_bits(acc[it][jt][4 * j + 0] + bv[it][j][0]);
+        const uint32_t h1 = bf16_rne_bits(acc[it][jt][4 * j + 1] + bv[it][j][1]);
+        const uint32_t h2 = bf16_rne_bits(acc[it][jt][4 * j + 2] + bv[it][j][2]);
+        const uint32_t h3 = bf16_rne_bits(acc[it][jt][4 * j + 3] + bv[it][j][3]);
+        *reinterpret_cast<uint2*>(stg + ml * kMxYRow + nl) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+      }
+  __syncthreads();
+
+  // 16-byte stores: thread t writes channels 8(t%16) .. +7 of tile rows t/16 + 16i
+  const int c8 = (tid & 15) * 8;
+  const int n = n0 + c8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = (tid >> 4) + 16 * i;
+    const int m = m0 + r;
+    if (m < M && n < N) {
+      const uint4 v = *reinterpret_cast<const uint4*>(stg + r * kMxYRow + c8);
+      uint16_t* dst = y + static_cast<size_t>(m) * N + n;
+      if ((N % 8) == 0) {
+        *reinterpret_cast<uint4*>(dst) = v;
+      } else {
+        const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (n + e < N) dst[e] = static_cast<uint16_t>(vv[e / 2] >> (16 * (e % 2)));
+      }
+    }
+  }
+}
 
 // One FP4 x FP4 MFMA over 64 k with per-lane block scales (byte 0 of sa, sb).
 __device__ __forceinline__ v16f mfma_fp4(const v4i& a, const v4i& b, const v16f& c, uint32_t sa, uint32_t sb) {
@@ -801,96 +655,238 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_mxfp4(
     if (st + 1 < S) iteration(st + 1, Slot<1>{});
   }
 
-  // up projection: acc += bf16(lora_act) . L2, 16 ranks per MFMA
-  for (int c0 = 0; c0 < rank; c0 += 16) {
-    const int j = c0 + 8 * h;
-    v4i ub[2], ua[2];
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt) {
-      const int m = m0 + wm * 64 + jt * 32 + l32;
-      ub[jt] = v4i{0, 0, 0, 0};
-      if (m < M) {
-        const float4* src = reinterpret_cast<const float4*>(lact + static_cast<size_t>(m) * rank + j);
-        const float4 f0 = src[0], f1 = src[1];
-        ub[jt] = v4i{static_cast<int>(pack_bf16_rne(f0.x, f0.y)), static_cast<int>(pack_bf16_rne(f0.z, f0.w)),
-                     static_cast<int>(pack_bf16_rne(f1.x, f1.y)), static_cast<int>(pack_bf16_rne(f1.z, f1.w))};
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int n = n0 + wn * 64 + it * 32 + l32;
-      ua[it] = n < N ? *reinterpret_cast<const v4i*>(lup + static_cast<size_t>(n) * rank + j) : v4i{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int it = 0; it < 2; ++it)
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
-        acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ua[it]),
-                                                              __builtin_bit_cast(v8bf, ub[jt]), acc[it][jt], 0, 0, 0);
+  epilogue_tile128(acc, reinterpret_cast<uint16_t*>(&lds_c[0][0]), lact, lup, bias, y, M, N, rank, n0, m0, wn, wm,
+                   l32, h, tid);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 2, INT4: 4-bit GEMM + per-group dequant + up projection + bias.
+//
+// Same tiling, two-slot pipeline and epilogue as the MXFP4 kernel: output
+// tile 128 (n) x 128 (m) per workgroup of 4 waves, 64 x 64 per wave.  A
+// stage is 128 k = two K-groups: per row 64 packed bytes and two fp16
+// scales.  The loader converts each 16 packed bytes to FP8 E4M3 subnormals
+// on their way into LDS (unpack_store_fp8: +-m * 2^-9 for the nibble s|mmm),
+// so that v_mfma_scale_f32_32x32x64_f8f6f4 returns the group's exact integer
+// partial P scaled by 2^(e_w + e_x) (exponents of the two scales applied as
+// E8M0 block scales, with 2^18 on the W side to cancel the code encoding).
+// The scale significands in [1, 2) multiply in packed fp16 and
+// v_fma_mix_f32 adds P' * (m_w m_x) into the fp32 accumulators.
+//
+// DEBUG = true is a test hook on the same loader, LDS layout and MFMA path:
+// unit scales, and the exact integer partial of every K-group written for a
+// window [win_m0, +win_mt) x [win_n0, +win_nt) of the output instead of Y.
+// ---------------------------------------------------------------------------
+constexpr int kI4Stage = 128;                 // k per pipeline stage (2 groups)
+constexpr int kI4Row = 2 * 64 + 16;           // LDS row stride: 128 FP8 codes + 16 bytes padding
+constexpr int kI4Slot = 2 * kTile * kI4Row;   // W rows, then X rows
+static_assert(2 * kI4Slot >= kTile * kMxYRow * 2, "output staging fits in the ring");
+
+template <bool DEBUG>
+__global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
+    const uint8_t* __restrict__ xq, const uint16_t* __restrict__ xs,
+    const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
+    const float* __restrict__ lact, const uint16_t* __restrict__ lup,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N, int K, int rank,
+    int win_m0, int win_n0, int win_mt, int win_nt, int32_t* __restrict__ dbg) {
+  __shared__ __attribute__((aligned(16))) int8_t lds_c[2][kI4Slot];
+  // per slot, operand (0 = W, 1 = X), group of the stage and row: the E8M0
+  // exponent byte of the scale and its fp16 significand
+  __shared__ __attribute__((aligned(16))) uint8_t lds_e[2][2][2][kTile];
+  __shared__ __attribute__((aligned(16))) _Float16 lds_m[2][2][2][kTile];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+  const int wn = wave >> 1, wm = wave & 1;
+  const int G = K / 64;
+  const int S = (G + 1) / 2;                   // the last stage holds one group when G is odd
+  const size_t kb = static_cast<size_t>(K / 2);
+
+  int n0, m0;
+  if constexpr (DEBUG) {
+    const int tiles_m = (win_mt + kTile - 1) / kTile;
+    n0 = win_n0 + (blockIdx.x / tiles_m) * kTile;
+    m0 = win_m0 + (blockIdx.x % tiles_m) * kTile;
+  } else {
+    const TileCoord tc = tile_coord(blockIdx.x, (N + kTile - 1) / kTile, (M + kTile - 1) / kTile);
+    n0 = tc.n0;
+    m0 = tc.m0;
   }
 
-  // bias (per channel: 4 consecutive channels per lane and 8-channel group)
-  float bv[2][4][4];
+  // code loads: rows wave*32 + 16i + lane/4 (i = 0, 1) of W and X, 16-byte
+  // chunk lane%4 of the stage's 64 bytes; rows clamped into the matrix
+  const int lr = wave * 32 + (lane >> 2), lc = lane & 3;
+  const uint8_t* wsrc0 = wq + static_cast<size_t>(min(n0 + lr, N - 1)) * kb + lc * 16;
+  const uint8_t* wsrc1 = wq + static_cast<size_t>(min(n0 + lr + 16, N - 1)) * kb + lc * 16;
+  const uint8_t* xsrc0 = xq + static_cast<size_t>(min(m0 + lr, M - 1)) * kb + lc * 16;
+  const uint8_t* xsrc1 = xq + static_cast<size_t>(min(m0 + lr + 16, M - 1)) * kb + lc * 16;
+  const int ldst = lr * kI4Row + lc * 32;
+  // scale loads: threads 0..127 W, 128..255 X; group (t/64)%2 of the stage,
+  // rows 2(t%64), 2(t%64)+1 (one dword where both rows are in the matrix
+  // and aligned, else two halves from rows clamped into the matrix)
+  const bool s_is_w = tid < kTile;
+  const int sg = (tid >> 6) & 1, sr = (tid & 63) * 2;
+  const int s_rows = s_is_w ? N : M;
+  const int s_r0 = (s_is_w ? n0 : m0) + sr;
+  const uint16_t* s_base = s_is_w ? ws : xs;
+  const bool s_dw = (s_rows % 2) == 0 && s_r0 + 1 < s_rows;
+
+  struct LoadRegs {
+    uint4 w0, w1, x0, x1;
+    uint32_t s;
+  };
+  // stage st; when its second group does not exist (odd G, last stage) the
+  // lanes of that group re-read the first one (never used)
+  auto gload = [&](int st) {
+    LoadRegs L;
+    const bool two = 2 * st + 1 < G;
+    const int off = st * (kI4Stage / 2) - (two || lc < 2 ? 0 : 32);
+    L.w0 = *reinterpret_cast<const uint4*>(wsrc0 + off);
+    L.w1 = *reinterpret_cast<const uint4*>(wsrc1 + off);
+    L.x0 = *reinterpret_cast<const uint4*>(xsrc0 + off);
+    L.x1 = *reinterpret_cast<const uint4*>(xsrc1 + off);
+    L.s = 0;
+    if constexpr (!DEBUG) {
+      const uint16_t* col = s_base + static_cast<size_t>(2 * st + (two ? sg : 0)) * s_rows;
+      if (s_dw) {
+        L.s = *reinterpret_cast<const uint32_t*>(col + s_r0);
+      } else {
+        L.s = static_cast<uint32_t>(col[min(s_r0, s_rows - 1)]) |
+              (static_cast<uint32_t>(col[min(s_r0 + 1, s_rows - 1)]) << 16);
+      }
+    }
+    return L;
+  };
+  // A scale s (fp16 >= 0) splits into its binary exponent, which the matrix
+  // core applies exactly as an E8M0 block scale, and its significand in
+  // [1, 2), an exact fp16; both from the fp32 image of s (normal for every
+  // fp16 value).  W rows carry an extra 2^18 that cancels the 2^-18 of the
+  // FP8 code encoding.  s == 0 gives byte 0 (2^-127) with significand 1;
+  // its codes are zero, so are its products.
+  auto lstore = [&](auto buf_c, LoadRegs L) {
+    constexpr int buf = decltype(buf_c)::value;
+    int8_t* wd = &lds_c[buf][0] + ldst;
+    int8_t* xd = &lds_c[buf][kTile * kI4Row] + ldst;
+    unpack_store_fp8(wd, L.w0);
+    unpack_store_fp8(wd + 16 * kI4Row, L.w1);
+    unpack_store_fp8(xd, L.x0);
+    unpack_store_fp8(xd + 16 * kI4Row, L.x1);
+    if constexpr (DEBUG) return;
+    uint32_t eb[2];
+    _Float16 sm[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t u = __float_as_uint(f16_bits_to_f32((L.s >> (16 * i)) & 0xFFFFu));
+      eb[i] = ((u >> 23) & 0xFFu) + (s_is_w && u != 0 ? 18u : 0u);
+      sm[i] = static_cast<_Float16>(__uint_as_float((u & 0x007FFFFFu) | 0x3F800000u));
+    }
+    *reinterpret_cast<uint16_t*>(&lds_e[buf][s_is_w ? 0 : 1][sg][sr]) = static_cast<uint16_t>(eb[0] | (eb[1] << 8));
+    *reinterpret_cast<h2*>(&lds_m[buf][s_is_w ? 0 : 1][sg][sr]) = h2{sm[0], sm[1]};
+  };
+
+  v16f acc[2][2];
 #pragma unroll
   for (int it = 0; it < 2; ++it)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int nb = n0 + wn * 64 + it * 32 + 8 * j + 4 * h;
+    for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bv[it][j][i] = 0.f;
-      if (bias) {
-        if ((N % 4) == 0 && nb + 3 < N) {
-          const uint2 b2 = *reinterpret_cast<const uint2*>(bias + nb);
-          bv[it][j][0] = __uint_as_float(b2.x << 16);
-          bv[it][j][1] = __uint_as_float(b2.x & 0xFFFF0000u);
-          bv[it][j][2] = __uint_as_float(b2.y << 16);
-          bv[it][j][3] = __uint_as_float(b2.y & 0xFFFF0000u);
-        } else {
+      for (int r = 0; r < 16; ++r) acc[it][jt][r] = 0.f;
+
+  // group g of the stage: FP8 bytes 64g + 32h of the row for lane half h
+  auto compute = [&](auto buf_c, bool one, int g0) {
+    constexpr int buf = decltype(buf_c)::value;
+    auto group = [&](auto g_c) {
+      constexpr int g = decltype(g_c)::value;
+      v8i a[2], b[2];
+      uint32_t ea[2], eb[2];
+      h2 mx2[2];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (nb + i < N) bv[it][j][i] = __uint_as_float(static_cast<uint32_t>(bias[nb + i]) << 16);
+      for (int t = 0; t < 2; ++t) {
+        const int8_t* wr = &lds_c[buf][0] + (wn * 64 + t * 32 + l32) * kI4Row + 64 * g + 32 * h;
+        const int8_t* xr = &lds_c[buf][kTile * kI4Row] + (wm * 64 + t * 32 + l32) * kI4Row + 64 * g + 32 * h;
+        a[t] = __builtin_shufflevector(*reinterpret_cast<const v4i*>(wr), *reinterpret_cast<const v4i*>(wr + 16), 0, 1,
+                                       2, 3, 4, 5, 6, 7);
+        b[t] = __builtin_shufflevector(*reinterpret_cast<const v4i*>(xr), *reinterpret_cast<const v4i*>(xr + 16), 0, 1,
+                                       2, 3, 4, 5, 6, 7);
+        ea[t] = lds_e[buf][0][g][wn * 64 + t * 32 + l32];
+        eb[t] = lds_e[buf][1][g][wm * 64 + t * 32 + l32];
+        const _Float16 mx = lds_m[buf][1][g][wm * 64 + t * 32 + l32];
+        mx2[t] = h2{mx, mx};
+      }
+      if constexpr (DEBUG) {
+#pragma unroll
+        for (int it = 0; it < 2; ++it)
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt) {
+            const v16f p =
+                __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[it], b[jt], v16f{}, 0, 0, 0, kUnitScales, 0,
+                                                                kUnitScales);
+            int32_t pi[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              pi[r] = static_cast<int32_t>(p[r] * 262144.0f);     // exact: P * 2^-18 * 2^18
+              asm volatile("" : "+v"(pi[r]));                    // read the MFMA result before the predicated stores
+            }
+            const int m = m0 + wm * 64 + jt * 32 + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int n = n0 + wn * 64 + it * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+              if (m < win_m0 + win_mt && n < win_n0 + win_nt)
+                dbg[(static_cast<size_t>(m - win_m0) * win_nt + (n - win_n0)) * G + g0 + g] = pi[r];
+            }
+          }
+        return;
+      }
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        // significands of the 4 consecutive W rows of lane elements 4j..4j+3
+        uint2 mw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          mw[j] = *reinterpret_cast<const uint2*>(&lds_m[buf][0][g][wn * 64 + it * 32 + 8 * j + 4 * h]);
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+          const v16f p =
+              __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[it], b[jt], v16f{}, 0, 0, 0, ea[it], 0, eb[jt]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const h2 s01 = __builtin_bit_cast(h2, mw[j].x) * mx2[jt];
+            const h2 s23 = __builtin_bit_cast(h2, mw[j].y) * mx2[jt];
+            acc[it][jt][4 * j + 0] = __builtin_fmaf(p[4 * j + 0], static_cast<float>(s01[0]), acc[it][jt][4 * j + 0]);
+            acc[it][jt][4 * j + 1] = __builtin_fmaf(p[4 * j + 1], static_cast<float>(s01[1]), acc[it][jt][4 * j + 1]);
+            acc[it][jt][4 * j + 2] = __builtin_fmaf(p[4 * j + 2], static_cast<float>(s23[0]), acc[it][jt][4 * j + 2]);
+            acc[it][jt][4 * j + 3] = __builtin_fmaf(p[4 * j + 3], static_cast<float>(s23[1]), acc[it][jt][4 * j + 3]);
+          }
         }
       }
-    }
+    };
+    group(Slot<0>{});
+    if (!one) group(Slot<1>{});
+  };
 
-  // Y = bf16(acc + bias), one rounding, into the staging tile [m][n]
-  uint16_t* stg = reinterpret_cast<uint16_t*>(&lds_c[0][0]);
-#pragma unroll
-  for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-    for (int it = 0; it < 2; ++it)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ml = wm * 64 + jt * 32 + l32;
-        const int nl = wn * 64 + it * 32 + 8 * j + 4 * h;
-        const uint32_t h0 = bf16_rne_bits(acc[it][jt][4 * j + 0] + bv[it][j][0]);
-        const uint32_t h1 = bf16_rne_bits(acc[it][jt][4 * j + 1] + bv[it][j][1]);
-        const uint32_t h2 = bf16_rne_bits(acc[it][jt][4 * j + 2] + bv[it][j][2]);
-        const uint32_t h3 = bf16_rne_bits(acc[it][jt][4 * j + 3] + bv[it][j][3]);
-        *reinterpret_cast<uint2*>(stg + ml * kMxYRow + nl) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-      }
+  LoadRegs ld = gload(0);
+  lstore(Slot<0>{}, ld);
+  if (S > 1) ld = gload(1);
   __syncthreads();
 
-  // 16-byte stores: thread t writes channels 8(t%16) .. +7 of tile rows t/16 + 16i
-  const int c8 = (tid & 15) * 8;
-  const int n = n0 + c8;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = (tid >> 4) + 16 * i;
-    const int m = m0 + r;
-    if (m < M && n < N) {
-      const uint4 v = *reinterpret_cast<const uint4*>(stg + r * kMxYRow + c8);
-      uint16_t* dst = y + static_cast<size_t>(m) * N + n;
-      if ((N % 8) == 0) {
-        *reinterpret_cast<uint4*>(dst) = v;
-      } else {
-        const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (n + e < N) dst[e] = static_cast<uint16_t>(vv[e / 2] >> (16 * (e % 2)));
-      }
-    }
+  auto iteration = [&](int st, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    if (st + 1 < S) lstore(Slot<1 - buf>{}, ld);
+    if (st + 2 < S) ld = gload(st + 2);
+    compute(buf_c, 2 * st + 1 >= G, 2 * st);
+    __syncthreads();
+  };
+  for (int st = 0; st < S; st += 2) {
+    iteration(st, Slot<0>{});
+    if (st + 1 < S) iteration(st + 1, Slot<1>{});
   }
+
+  if constexpr (!DEBUG)
+    epilogue_tile128(acc, reinterpret_cast<uint16_t*>(&lds_c[0][0]), lact, lup, bias, y, M, N, rank, n0, m0, wn, wm,
+                     l32, h, tid);
 }
 
 // K1 grid: 64-row blocks x K slices.  The slice count is chosen so that
@@ -1006,9 +1002,9 @@ hipError_t launch_unfused(const void* x, int M, int K, const float* sinv, const 
     if (e != hipSuccess) return e;
   }
   const int tiles = ((N + kTile - 1) / kTile) * ((M + kTile - 1) / kTile);               // 3: 4-bit GEMM
-  hipLaunchKernelGGL(k2_gemm_w4a4<false>, dim3(tiles), dim3(kK2Threads), 0, st, xq,
-                     static_cast<const uint16_t*>(xs), wq, static_cast<const uint16_t*>(ws), nullptr, nullptr,
-                     nullptr, static_cast<uint16_t*>(y), M, N, K, 0, 0, 0, 0, 0, nullptr);
+  hipLaunchKernelGGL(k2_gemm_int4<false>, dim3(tiles), dim3(kMxThreads), 0, st, xq, static_cast<const uint16_t*>(xs),
+                     wq, static_cast<const uint16_t*>(ws), nullptr, nullptr, nullptr, static_cast<uint16_t*>(y), M, N,
+                     K, 0, 0, 0, 0, 0, nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_up_proj, dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, st, lact,  // 4: up projection
                      static_cast<const uint16_t*>(lup), static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y),
@@ -1053,7 +1049,7 @@ extern "C" int svdq_launch_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs, 
                        static_cast<uint16_t*>(y), M, N, K, rank);
     return static_cast<int>(hipGetLastError());
   }
-  hipLaunchKernelGGL(k2_gemm_w4a4<false>, dim3(tiles), dim3(kK2Threads), 0, static_cast<hipStream_t>(stream), xq,
+  hipLaunchKernelGGL(k2_gemm_int4<false>, dim3(tiles), dim3(kMxThreads), 0, static_cast<hipStream_t>(stream), xq,
                      static_cast<const uint16_t*>(xs), wq, static_cast<const uint16_t*>(ws), lora_act,
                      static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias),
                      static_cast<uint16_t*>(y), M, N, K, rank, 0, 0, 0, 0, nullptr);
@@ -1085,7 +1081,7 @@ extern "C" int svdq_launch_unfused_linear(const void* x, int M, int K, const flo
 extern "C" int svdq_launch_debug_group_partials(const uint8_t* xq, const uint8_t* wq, int M, int N, int K, int m0,
                                                 int n0, int mt, int nt, int32_t* out, void* stream) {
   const int tiles = ((nt + kTile - 1) / kTile) * ((mt + kTile - 1) / kTile);
-  hipLaunchKernelGGL(k2_gemm_w4a4<true>, dim3(tiles), dim3(kK2Threads), 0, static_cast<hipStream_t>(stream), xq, nullptr,
-                     wq, nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, 0, m0, n0, mt, nt, out);
+  hipLaunchKernelGGL(k2_gemm_int4<true>, dim3(tiles), dim3(kMxThreads), 0, static_cast<hipStream_t>(stream), xq,
+                     nullptr, wq, nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, 0, m0, n0, mt, nt, out);
   return static_cast<int>(hipGetLastError());
 }
