@@ -25,7 +25,7 @@ from ._lib import (INT4, MXFP4, SVDQ_ERR_HIP, SVDQ_ERR_INVALID_ARG,  # noqa: F40
                    EXPORTED, LIB_PATH, SvdqError, check, lib, status_string)
 
 __all__ = [
-    "INT4", "MXFP4", "SvdqError", "lib", "LIB_PATH", "status_string",
+    "INT4", "MXFP4", "SvdqError", "lib", "LIB_PATH", "status_string", "merge_lora",
     "version", "device_check", "packed_sizes", "act_sizes", "pack_weights",
     "quantize_act_lora_down", "gemm_w4a4_lora_up", "debug_group_partials", "unfused_linear",
     "PackedLinear", "linear",
@@ -85,6 +85,32 @@ def pack_weights(w_bf16: np.ndarray, act_absmax: np.ndarray, rank: int,
     if want_residual:
         out["r"] = r
     return out
+
+
+def merge_lora(lora_down: Optional[np.ndarray], lora_up: Optional[np.ndarray], smooth_inv: np.ndarray,
+               a_bf16: np.ndarray, b_bf16: np.ndarray):
+    """Merge an off-the-shelf LoRA (Y += X A B) into the packed 16-bit branch
+    on the CPU, leaving the 4-bit residual as it is.  lora_down [rank][K] and
+    lora_up [N][rank] are bf16 bits from pack_weights (None for rank 0);
+    a_bf16 [K][ra], b_bf16 [ra][N] bf16 bits.  Returns (lora_down'
+    [rank+ra][K], lora_up' [N][rank+ra])."""
+    sinv = np.ascontiguousarray(smooth_inv, dtype=np.float32)
+    a = np.ascontiguousarray(a_bf16, dtype=np.uint16)
+    b = np.ascontiguousarray(b_bf16, dtype=np.uint16)
+    K, ra = a.shape
+    N = b.shape[1]
+    if b.shape[0] != ra or sinv.shape != (K,):
+        raise ValueError("a must be [K][ra], b [ra][N] and smooth_inv [K]")
+    rank = 0 if lora_down is None else int(np.asarray(lora_down).shape[0])
+    ld = None if rank == 0 else np.ascontiguousarray(lora_down, dtype=np.uint16)
+    lu = None if rank == 0 else np.ascontiguousarray(lora_up, dtype=np.uint16)
+    if rank and (ld.shape != (rank, K) or lu.shape != (N, rank)):
+        raise ValueError("lora_down must be [rank][K] and lora_up [N][rank]")
+    down = np.empty((rank + ra, K), np.uint16)
+    up = np.empty((N, rank + ra), np.uint16)
+    check(lib.svdq_merge_lora(_np_ptr(ld), _np_ptr(lu), rank, _np_ptr(sinv), _np_ptr(a), _np_ptr(b), ra, K, N,
+                              _np_ptr(down), _np_ptr(up)))
+    return down, up
 
 
 # ---------------------------------------------------------------------------

@@ -840,28 +840,39 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
           }
         return;
       }
+      // significands of the 4 consecutive W rows of lane elements 4j..4j+3
+      uint2 mw[2][4];
 #pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        // significands of the 4 consecutive W rows of lane elements 4j..4j+3
-        uint2 mw[4];
+      for (int it = 0; it < 2; ++it)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          mw[j] = *reinterpret_cast<const uint2*>(&lds_m[buf][0][g][wn * 64 + it * 32 + 8 * j + 4 * h]);
+          mw[it][j] = *reinterpret_cast<const uint2*>(&lds_m[buf][0][g][wn * 64 + it * 32 + 8 * j + 4 * h]);
+      auto mf = [&](int t) {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[t >> 1], b[t & 1], v16f{}, 0, 0, 0, ea[t >> 1], 0,
+                                                               eb[t & 1]);
+      };
+      auto dq = [&](int t, const v16f& p) {
+        const int it = t >> 1, jt = t & 1;
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          const v16f p =
-              __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[it], b[jt], v16f{}, 0, 0, 0, ea[it], 0, eb[jt]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const h2 s01 = __builtin_bit_cast(h2, mw[j].x) * mx2[jt];
-            const h2 s23 = __builtin_bit_cast(h2, mw[j].y) * mx2[jt];
-            acc[it][jt][4 * j + 0] = __builtin_fmaf(p[4 * j + 0], static_cast<float>(s01[0]), acc[it][jt][4 * j + 0]);
-            acc[it][jt][4 * j + 1] = __builtin_fmaf(p[4 * j + 1], static_cast<float>(s01[1]), acc[it][jt][4 * j + 1]);
-            acc[it][jt][4 * j + 2] = __builtin_fmaf(p[4 * j + 2], static_cast<float>(s23[0]), acc[it][jt][4 * j + 2]);
-            acc[it][jt][4 * j + 3] = __builtin_fmaf(p[4 * j + 3], static_cast<float>(s23[1]), acc[it][jt][4 * j + 3]);
-          }
+        for (int j = 0; j < 4; ++j) {
+          const h2 s01 = __builtin_bit_cast(h2, mw[it][j].x) * mx2[jt];
+          const h2 s23 = __builtin_bit_cast(h2, mw[it][j].y) * mx2[jt];
+          acc[it][jt][4 * j + 0] = __builtin_fmaf(p[4 * j + 0], static_cast<float>(s01[0]), acc[it][jt][4 * j + 0]);
+          acc[it][jt][4 * j + 1] = __builtin_fmaf(p[4 * j + 1], static_cast<float>(s01[1]), acc[it][jt][4 * j + 1]);
+          acc[it][jt][4 * j + 2] = __builtin_fmaf(p[4 * j + 2], static_cast<float>(s23[0]), acc[it][jt][4 * j + 2]);
+          acc[it][jt][4 * j + 3] = __builtin_fmaf(p[4 * j + 3], static_cast<float>(s23[1]), acc[it][jt][4 * j + 3]);
         }
-      }
+      };
+      // software pipeline: the MFMA of tile t+1 is issued before the
+      // dequant of tile t, so that the matrix core and the VALU overlap
+      v16f p0 = mf(0);
+      v16f p1 = mf(1);
+      dq(0, p0);
+      p0 = mf(2);
+      dq(1, p1);
+      p1 = mf(3);
+      dq(2, p0);
+      dq(3, p1);
     };
     group(Slot<0>{});
     if (!one) group(Slot<1>{});

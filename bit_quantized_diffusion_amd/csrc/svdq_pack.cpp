@@ -542,3 +542,40 @@ extern "C" int svdq_pack_weights(const uint16_t* w_bf16, const float* act_absmax
   }
   return SVDQ_OK;
 }
+
+// Off-the-shelf LoRA merged into the 16-bit branch without re-quantizing
+// the residual (SVDQuant abstract: the engine supports low-rank adapters
+// without re-quantization).  The branch reads X^ = X diag(smooth_inv), so
+// the adapter's down factor is folded with 1/smooth_inv:
+// L1' = [L1 | A diag(1/smooth_inv)], L2' = [L2 ; B]; then X^ L1' L2' =
+// X^ L1 L2 + X A B.  Each folded element is a[k][j] / smooth_inv[k] in fp64,
+// rounded to fp32 and then to bf16 (nearest even).
+extern "C" int svdq_merge_lora(const uint16_t* lora_down, const uint16_t* lora_up, int rank,
+                               const float* smooth_inv, const uint16_t* a, const uint16_t* b, int lora_rank, int K,
+                               int N, uint16_t* lora_down_out, uint16_t* lora_up_out) {
+  if (!smooth_inv || !a || !b || !lora_down_out || !lora_up_out) return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!lora_down || !lora_up)) return SVDQ_ERR_INVALID_ARG;
+  if (K < 1 || N < 1 || lora_rank < 1 || rank < 0) return SVDQ_ERR_SHAPE;
+  int st;
+  if ((st = check_rank(rank, K, N))) return st;
+  if ((st = check_rank(rank + lora_rank, K, N))) return st;
+  const int r2 = rank + lora_rank;
+  const int64_t k64 = K;
+  // L1'^T = [L1^T ; (A diag(1/smooth_inv))^T]: rows 0..rank-1 copied
+  if (rank > 0) std::memcpy(lora_down_out, lora_down, sizeof(uint16_t) * static_cast<size_t>(rank) * K);
+  for (int j = 0; j < lora_rank; ++j) {
+    uint16_t* dst = lora_down_out + static_cast<int64_t>(rank + j) * k64;
+    for (int k = 0; k < K; ++k) {
+      const double v = static_cast<double>(bf16_bits_to_f32(a[static_cast<int64_t>(k) * lora_rank + j])) /
+                       static_cast<double>(smooth_inv[k]);
+      dst[k] = f32_to_bf16_bits(static_cast<float>(v));
+    }
+  }
+  // L2'^T [N][r2] = [L2^T | B^T]
+  for (int n = 0; n < N; ++n) {
+    uint16_t* dst = lora_up_out + static_cast<int64_t>(n) * r2;
+    for (int c = 0; c < rank; ++c) dst[c] = lora_up[static_cast<int64_t>(n) * rank + c];
+    for (int j = 0; j < lora_rank; ++j) dst[rank + j] = b[static_cast<int64_t>(j) * N + n];
+  }
+  return SVDQ_OK;
+}

@@ -122,6 +122,28 @@ SVDQ_API int svdq_pack_weights(const uint16_t* w_bf16, const float* act_absmax,
                       float* smooth_inv, uint16_t* lora_down, uint16_t* lora_up,
                       uint8_t* wq, void* ws, float* r_out);
 
+/* Merge an off-the-shelf LoRA (Y += X A B) into the packed 16-bit branch,
+ * on the CPU, without touching the 4-bit residual (SVDQuant abstract: the
+ * engine supports low-rank adapters without re-quantization).  The branch
+ * reads X^ = X diag(smooth_inv), so A is folded with 1/smooth_inv:
+ * L1' = [L1 | A diag(1/smooth_inv)], L2' = [L2 ; B]; each folded element is
+ * a[k][j] / smooth_inv[k] in fp64, rounded to fp32, then to bf16 (RNE).
+ *
+ *   lora_down      [rank][K] bf16        from svdq_pack_weights; NULL if rank == 0
+ *   lora_up        [N][rank] bf16        from svdq_pack_weights; NULL if rank == 0
+ *   smooth_inv     [K] fp32              from svdq_pack_weights
+ *   a              [K][lora_rank] bf16   adapter down factor
+ *   b              [lora_rank][N] bf16   adapter up factor
+ *   lora_down_out  [rank+lora_rank][K] bf16, out (caller-allocated)
+ *   lora_up_out    [N][rank+lora_rank] bf16, out (caller-allocated)
+ * rank + lora_rank must meet the hot calls' rank rule (a multiple of 16, at
+ * most 256 and at most min(K, N)), else SVDQ_ERR_SHAPE.  All pointers host;
+ * the outputs must not overlap the inputs. */
+SVDQ_API int svdq_merge_lora(const uint16_t* lora_down, const uint16_t* lora_up, int rank,
+                             const float* smooth_inv, const uint16_t* a, const uint16_t* b,
+                             int lora_rank, int K, int N,
+                             uint16_t* lora_down_out, uint16_t* lora_up_out);
+
 /* Fused kernel 1 (Nunchaku engine caption (b): the down projection and the
  * quantizer share their input, so X is read once).
  *

@@ -12,6 +12,7 @@ import torch
 
 import bit_quantized_diffusion_amd as bq
 import oracle as O
+import synth
 from tests import _cases as C
 
 pytestmark = pytest.mark.gpu
@@ -302,3 +303,29 @@ def test_full_size_layer(name):
     rows = _sample_rows(M)
     ref = C.oracle_rows(case, rows)
     assert_y_close(host_u16(y)[rows], ref["y"], f"{name} end to end")
+
+
+def test_layer_with_merged_lora():
+    """A rank-32 layer with a rank-16 adapter merged by the library's host
+    call (svdq_merge_lora): the rank-48 hot path against the oracle of the
+    merged layer."""
+    spec_case = C.small_case(200, 768, 264, 32, 21, True, 16)
+    x = spec_case["x"]
+    M, K = x.shape
+    lay_pk = spec_case["pk"]          # oracle-packed, LoRA merged by the oracle
+    say("merged LoRA layer")
+    # the library's merge of the same adapter onto the same unmerged factors
+    spec = spec_case["spec"]
+    a_bits, b_bits = synth.gen_lora(spec)
+    base = O.pack_weights(spec_case["w"], spec_case["ax"], 32)
+    down, up = bq.merge_lora(np.ascontiguousarray(base["l1"].T), np.ascontiguousarray(base["l2"].T),
+                             base["smooth_inv"], a_bits, b_bits)
+    assert np.array_equal(down, np.ascontiguousarray(lay_pk["l1"].T))
+    assert np.array_equal(up, np.ascontiguousarray(lay_pk["l2"].T))
+    layer = bq.PackedLinear(K=K, N=base["wq"].shape[0], rank=48, precision=bq.INT4,
+                            smooth_inv=dev(base["smooth_inv"]), lora_down=dev_bf16(down), lora_up=dev_bf16(up),
+                            wq=dev(base["wq"]), ws=dev(base["ws"]), bias=dev_bf16(spec_case["bias"]))
+    ref = C.oracle_rows(spec_case, np.arange(M))
+    y = bq.linear(dev_bf16(x), layer)
+    torch.cuda.synchronize()
+    assert_y_close(host_u16(y), ref["y"], "merged lora")

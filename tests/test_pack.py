@@ -108,3 +108,53 @@ def test_pack_is_deterministic():
     b = bq.pack_weights(lay["w"], ax, 32)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+# ---------------------------------------------------------------------------
+# LoRA merge (host entry point) against the oracle's merge
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rank,lora_rank", [(16, 16), (0, 16), (32, 32)])
+def test_merge_lora_bit_exact(rank, lora_rank):
+    """Same concatenation and the same fp64 fold with 1/smooth_inv, rounded
+    once to fp32 then to bf16: bit for bit the oracle's merge."""
+    spec = synth.custom_spec(40, 256, 96, rank, seed=7, lora_rank=lora_rank)
+    lay, ax = _layer(spec)
+    pk = bq.pack_weights(lay["w"], ax, rank)
+    a_bits, b_bits = synth.gen_lora(spec)
+    down, up = bq.merge_lora(pk["lora_down"] if rank else None, pk["lora_up"] if rank else None,
+                             pk["smooth_inv"], a_bits, b_bits)
+    l1 = np.ascontiguousarray(pk["lora_down"].T) if rank else np.zeros((spec.K, 0), np.uint16)
+    l2 = np.ascontiguousarray(pk["lora_up"].T) if rank else np.zeros((0, spec.N), np.uint16)
+    l1n, l2n = O.merge_lora(l1, l2, pk["smooth_inv"], a_bits, b_bits)
+    assert down.shape == (rank + lora_rank, spec.K) and up.shape == (spec.N, rank + lora_rank)
+    assert np.array_equal(down, np.ascontiguousarray(l1n.T))
+    assert np.array_equal(up, np.ascontiguousarray(l2n.T))
+
+
+def test_merge_lora_adds_the_adapter():
+    """The merged branch adds X A B (up to the bf16 roundings of the fold):
+    X^ L1' L2' - X^ L1 L2 = X A B."""
+    spec = synth.custom_spec(32, 256, 64, 16, seed=8, lora_rank=16)
+    lay, ax = _layer(spec)
+    pk = bq.pack_weights(lay["w"], ax, 16)
+    a_bits, b_bits = synth.gen_lora(spec)
+    down, up = bq.merge_lora(pk["lora_down"], pk["lora_up"], pk["smooth_inv"], a_bits, b_bits)
+    x = O.bf16_bits_to_f32(lay["x"]).astype(np.float64)
+    xh = x * pk["smooth_inv"].astype(np.float64)[None, :]
+    f = lambda t: O.bf16_bits_to_f32(t).astype(np.float64)
+    delta = xh @ f(down.T) @ f(up.T) - xh @ f(pk["lora_down"].T) @ f(pk["lora_up"].T)
+    want = x @ f(a_bits) @ f(b_bits)
+    assert np.max(np.abs(delta - want)) <= 1e-2 * np.max(np.abs(want))
+
+
+def test_merge_lora_rejects_bad_arguments():
+    K, N = 128, 64
+    sinv = np.ones(K, np.float32)
+    a = np.zeros((K, 8), np.uint16)
+    b = np.zeros((8, N), np.uint16)
+    with pytest.raises(bq.SvdqError) as e:        # merged rank 8 is not a multiple of 16
+        bq.merge_lora(None, None, sinv, a, b)
+    assert e.value.status == bq.SVDQ_ERR_SHAPE
+    st = bq.lib.svdq_merge_lora(None, None, 0, None, None, None, 16, K, N, None, None)
+    assert st == bq.SVDQ_ERR_INVALID_ARG
