@@ -201,18 +201,21 @@ __global__ __launch_bounds__(256) void k1_quant_down_int4(
       const uint32_t sbits = f16_sat_bits(__fdiv_rn(amax, 7.0f));
       const float s = f16_bits_to_f32(sbits);
       const float inv = (s == 0.f) ? 0.f : __fdiv_rn(1.0f, s);
+      // 8 codes per word: each code as the byte s000_0mmm (sign of a
+      // negative code in bit 7, |q| in bits 0-2), E = the even-k bytes,
+      // O = the odd-k bytes, word = E | rotl32(O, 4)
       uint32_t word[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        word[c] = 0;
+        uint32_t eo[2] = {0u, 0u};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float qf = __builtin_rintf(xh[c][e] * inv);
           qf = fminf(7.f, fmaxf(-7.f, qf));
-          // sign-magnitude nibble: bit 3 = sign, bits 0-2 = |q| (zero stays 0)
-          const uint32_t nib = static_cast<uint32_t>(static_cast<int>(fabsf(qf))) | (qf < 0.f ? 8u : 0u);
-          word[c] |= nib << (4 * e);
+          const uint32_t b = static_cast<uint32_t>(static_cast<int>(fabsf(qf))) | (qf < 0.f ? 0x80u : 0u);
+          eo[e & 1] |= b << (8 * (e >> 1));
         }
+        word[c] = eo[0] | __builtin_amdgcn_alignbit(eo[1], eo[1], 28);
       }
       // the lane's 32 codes are 16 contiguous bytes of the packed row
       if (row_ok && valid)
@@ -308,8 +311,9 @@ __global__ void fill_zero_f32(float* __restrict__ p, size_t n) {
 // channels of one token; the epilogue turns the tile around in LDS so that
 // Y is written in 16-byte row segments.
 //
-// INT4 codes reach the matrix core as FP8 E4M3 subnormals: a sign-magnitude
-// nibble s|mmm becomes the byte s000_0mmm, which is exactly +-m * 2^-9.  For
+// INT4 codes reach the matrix core as FP8 E4M3 subnormals: a code q becomes
+// the byte s000_0mmm (sign, |q|), which is exactly q * 2^-9; the packed
+// layout keeps those bytes two masks away (unpack_store_fp8).  For
 // one K-group of 64, v_mfma_scale_f32_32x32x64_f8f6f4 then returns the
 // group's integer partial P times 2^-18 times its two E8M0 block scales,
 // exactly: every product is a multiple of 2^-18 and every partial sum stays
@@ -352,16 +356,18 @@ __device__ __forceinline__ TileCoord tile_coord(int pid, int tiles_n, int tiles_
   return tc;
 }
 
-// 16 packed bytes (32 sign-magnitude nibbles) -> 32 FP8 E4M3 bytes.  The
-// even codes of each packed dword go to one output dword, the odd codes to
-// the next: a fixed permutation of k that A and B share.
+// 16 packed bytes (32 codes) -> 32 FP8 E4M3 bytes.  A packed word is
+// E | rotl32(O, 4) with E and O the FP8 images (s000_0mmm) of its 4 even-k
+// and 4 odd-k codes, so E = w & 0x87878787 and O = rotr32(w, 4) &
+// 0x87878787.  E goes to one output dword and O to the next: a fixed
+// permutation of k that A and B share.
 __device__ __forceinline__ void unpack_store_fp8(int8_t* dst, const uint4& w) {
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
   uint32_t o[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    o[2 * i] = ((ws[i] & 0x08080808u) << 4) | (ws[i] & 0x07070707u);
-    o[2 * i + 1] = ((ws[i] >> 4) & 0x07070707u) | (ws[i] & 0x80808080u);
+    o[2 * i] = ws[i] & 0x87878787u;
+    o[2 * i + 1] = __builtin_amdgcn_alignbit(ws[i], ws[i], 4) & 0x87878787u;
   }
   uint4* d = reinterpret_cast<uint4*>(dst);
   d[0] = make_uint4(o[0], o[1], o[2], o[3]);
@@ -666,7 +672,7 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_mxfp4(
 // tile 128 (n) x 128 (m) per workgroup of 4 waves, 64 x 64 per wave.  A
 // stage is 128 k = two K-groups: per row 64 packed bytes and two fp16
 // scales.  The loader converts each 16 packed bytes to FP8 E4M3 subnormals
-// on their way into LDS (unpack_store_fp8: +-m * 2^-9 for the nibble s|mmm),
+// on their way into LDS (unpack_store_fp8: q * 2^-9 for the code q),
 // so that v_mfma_scale_f32_32x32x64_f8f6f4 returns the group's exact integer
 // partial P scaled by 2^(e_w + e_x) (exponents of the two scales applied as
 // E8M0 block scales, with 2^18 on the W side to cancel the code encoding).

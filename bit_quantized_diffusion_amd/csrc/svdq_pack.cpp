@@ -374,15 +374,20 @@ void quant_int4_row(const float* v, int K, uint8_t* q_packed, uint16_t* scale_bi
       continue;
     }
     const float inv = 1.0f / s;
-    for (int i = 0; i < kInt4Group; i += 2) {
-      int q0 = static_cast<int>(std::nearbyint(gv[i] * inv));
-      int q1 = static_cast<int>(std::nearbyint(gv[i + 1] * inv));
-      q0 = std::min(7, std::max(-7, q0));
-      q1 = std::min(7, std::max(-7, q1));
-      // sign-magnitude nibbles: bit 3 = sign, bits 0-2 = |q|
-      const int n0 = q0 < 0 ? (8 | -q0) : q0;
-      const int n1 = q1 < 0 ? (8 | -q1) : q1;
-      out[i / 2] = static_cast<uint8_t>(n0 | (n1 << 4));
+    // 8 codes per little-endian word: each code as the byte s000_0mmm,
+    // E = the even-k bytes, O = the odd-k bytes, word = E | rotl32(O, 4)
+    for (int i = 0; i < kInt4Group; i += 8) {
+      uint32_t e = 0, o = 0;
+      for (int j = 0; j < 4; ++j) {
+        int q0 = static_cast<int>(std::nearbyint(gv[i + 2 * j] * inv));
+        int q1 = static_cast<int>(std::nearbyint(gv[i + 2 * j + 1] * inv));
+        q0 = std::min(7, std::max(-7, q0));
+        q1 = std::min(7, std::max(-7, q1));
+        e |= static_cast<uint32_t>(q0 < 0 ? (0x80 | -q0) : q0) << (8 * j);
+        o |= static_cast<uint32_t>(q1 < 0 ? (0x80 | -q1) : q1) << (8 * j);
+      }
+      const uint32_t word = e | (o << 4) | (o >> 28);
+      for (int b = 0; b < 4; ++b) out[i / 2 + b] = static_cast<uint8_t>(word >> (8 * b));
     }
   }
 }

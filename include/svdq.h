@@ -32,11 +32,16 @@
  *    stored the same way: lora_down = L1^T as [rank][K] and lora_up = L2^T
  *    as [N][rank], i.e. the weights of the two small linears K->rank and
  *    rank->N.
- *  - INT4 codes: sign-magnitude nibbles (bit 3 = sign, bits 0-2 = |q|,
- *    q in [-7, 7], zero stored as 0), code k in the low nibble of byte k/2
- *    when k is even; rows of K/2 bytes.
+ *  - INT4 codes, q in [-7, 7]: 4 bits each, rows of K/2 bytes, 8
+ *    consecutive k per little-endian 32-bit word.  Each code taken as the
+ *    byte s000_0mmm (bit 7 = sign of a negative code, bits 0-2 = |q|), E =
+ *    the word of the 4 even-k bytes (byte j = k 8w+2j), O = that of the 4
+ *    odd-k bytes; the stored word is E | rotl32(O, 4).  (So byte j holds
+ *    |e_j| in bits 0-2, its sign in bit 7, |o_j| in bits 4-6 and the sign of
+ *    o_(j+3)%4 in bit 3; E = w & 0x87878787, O = rotr32(w, 4) & 0x87878787.)
  *    INT4 scales: fp16, one per 64 consecutive k of a row, group-major
- *    [K/64][rows].  MXFP4 codes: E2M1 nibbles (sign in bit 3), same packing;
+ *    [K/64][rows].  MXFP4 codes: E2M1 nibbles (sign in bit 3), code k in
+ *    the low nibble of byte k/2 when k is even;
  *    MXFP4 scales: E8M0 bytes, one per 32 k, group-major [K/32][rows].
  *  - Shapes: M, N >= 1 (any value); K >= 64 and K % 64 == 0 for INT4,
  *    K % 128 == 0 for MXFP4; rank == 0 (no low-rank branch) or a multiple of

@@ -129,22 +129,51 @@ def quantize_groups(v):
     return q.reshape(rows, K), s
 
 
-def pack_int4(q) -> np.ndarray:
-    """int8 codes [rows][K] in [-7, 7] -> uint8 [rows][K/2] (reading R6):
-    sign-magnitude nibbles, code k in the low nibble of byte k/2 when k is
-    even."""
+def _code_bytes(q) -> np.ndarray:
+    """int codes in [-7, 7] -> the byte s000_0mmm (bit 7 set for a negative
+    code, bits 0-2 = |q|; zero carries no sign)."""
     q = np.asarray(q).astype(np.int16)
-    assert np.all(np.abs(q) <= 7), "sign-magnitude nibbles hold [-7, 7]"
-    u = np.where(q < 0, 8 | (-q), q).astype(np.uint8)
-    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+    assert np.all(np.abs(q) <= 7), "4-bit codes hold [-7, 7]"
+    return np.where(q < 0, 0x80 | (-q), q).astype(np.uint32)
+
+
+def pack_int4(q) -> np.ndarray:
+    """int8 codes [rows][K] (K % 8 == 0) in [-7, 7] -> uint8 [rows][K/2]
+    (reading R6).  Each little-endian 32-bit word holds 8 consecutive k.
+    With E the word whose byte j is the code byte of k = 8w + 2j and O the
+    word of the odd k = 8w + 2j + 1, the stored word is E | rotl32(O, 4):
+    byte j keeps |e_j| in bits 0-2 and its sign in bit 7, |o_j| in bits 4-6,
+    and bit 3 carries the sign of o_{(j+3) % 4}."""
+    b = _code_bytes(q)
+    rows, K = b.shape
+    assert K % 8 == 0
+    b = b.reshape(rows, K // 8, 4, 2)
+    E = np.zeros((rows, K // 8), np.uint64)
+    O = np.zeros((rows, K // 8), np.uint64)
+    for j in range(4):
+        E |= b[:, :, j, 0].astype(np.uint64) << np.uint64(8 * j)
+        O |= b[:, :, j, 1].astype(np.uint64) << np.uint64(8 * j)
+    rot = ((O << np.uint64(4)) | (O >> np.uint64(28))) & np.uint64(0xFFFFFFFF)
+    words = (E | rot).astype("<u4")
+    return np.ascontiguousarray(words).view(np.uint8).reshape(rows, K // 2)
 
 
 def unpack_int4(p) -> np.ndarray:
-    p = np.asarray(p, dtype=np.uint8)
-    out = np.empty((p.shape[0], p.shape[1] * 2), dtype=np.int8)
-    for sl, nib in ((slice(0, None, 2), p & 0xF), (slice(1, None, 2), p >> 4)):
-        mag = (nib & 7).astype(np.int8)
-        out[:, sl] = np.where(nib & 8, -mag, mag)
+    """Inverse of pack_int4: E = w & 0x87878787, O = rotr32(w, 4) &
+    0x87878787, each byte read as sign (bit 7) and magnitude (bits 0-2)."""
+    p = np.ascontiguousarray(p, dtype=np.uint8)
+    rows, nb = p.shape
+    assert nb % 4 == 0
+    w = p.view("<u4").astype(np.uint64)
+    mask = np.uint64(0x87878787)
+    E = w & mask
+    O = ((w >> np.uint64(4)) | (w << np.uint64(28))) & mask
+    out = np.empty((rows, nb * 2), dtype=np.int8)
+    for j in range(4):
+        for parity, X in ((0, E), (1, O)):
+            byte = (X >> np.uint64(8 * j)) & np.uint64(0xFF)
+            mag = (byte & np.uint64(7)).astype(np.int8)
+            out[:, 2 * j + parity::8] = np.where(byte & np.uint64(0x80), -mag, mag)
     return out
 
 

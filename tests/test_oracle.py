@@ -195,15 +195,18 @@ def test_quantizer_error_bound():
 
 
 def test_pack_bytes_and_roundtrip():
-    # sign-magnitude nibbles: -1 -> 0x9, -7 -> 0xF, -5 -> 0xD, -3 -> 0xB
+    # code bytes: 1 -> 0x01, -1 -> 0x81, -7 -> 0x87, 7 -> 0x07, 0 -> 0x00,
+    # -5 -> 0x85, 3 -> 0x03, -3 -> 0x83.  E (k even) = 0x03008701, O (k odd)
+    # = 0x83850781, rotl32(O, 4) = 0x38507818, E | rotl = 0x3b50ff19, stored
+    # little-endian
     q = np.array([[1, -1, -7, 7, 0, -5, 3, -3]], dtype=np.int8)
     p = O.pack_int4(q)
-    assert list(p[0]) == [0x91, 0x7F, 0xD0, 0xB3]
+    assert list(p[0]) == [0x19, 0xFF, 0x50, 0x3B]
     rng = np.random.default_rng(1)
     q = rng.integers(-7, 8, (9, 128)).astype(np.int8)
     assert np.array_equal(O.unpack_int4(O.pack_int4(q)), q)
-    # a negative zero nibble decodes to 0
-    assert O.unpack_int4(np.array([[0x88]], np.uint8)).tolist() == [[0, 0]]
+    # sign bits on zero magnitudes decode to 0
+    assert O.unpack_int4(np.array([[0x88, 0x88, 0x88, 0x88]], np.uint8)).tolist() == [[0] * 8]
 
 
 # ---------------------------------------------------------------------------
