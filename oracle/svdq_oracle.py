@@ -36,10 +36,12 @@ both this oracle and the GPU path):
       s = fp16(fp32(amax / 7)) with round-to-nearest-even and saturation at
       65504; s == 0 -> all codes 0; otherwise inv = fp32(1/s) and
       q = clamp(rint(fp32(v * inv)), -7, 7), ties to even.
-  R6  codes are sign-magnitude nibbles (bit 3 = sign, bits 0-2 = |q|; zero
-      is stored as 0), low nibble = even k, row-major [rows][K/2]; scales
-      are group-major [K/64][rows].  Sign-magnitude holds exactly the
-      symmetric range [-7, 7] of the quantizer.
+  R6  codes take 4 bits each, row-major [rows][K/2], 8 consecutive k per
+      little-endian 32-bit word: with each code as the byte s000_0mmm
+      (sign of a negative code in bit 7, |q| in bits 0-2), E the word of
+      the 4 even-k bytes and O that of the 4 odd-k bytes, the word is
+      E | rotl32(O, 4).  Sign and magnitude hold exactly the symmetric
+      range [-7, 7] of the quantizer.  Scales are group-major [K/64][rows].
   R7  x^ = bf16(fp32(x * smooth_inv)), rounded once and used by both branches.
   R8  down projection t = X^ L1 in fp64 (the GPU keeps it in fp32 [M][r]);
       the up projection uses bf16(fp32(t)).
