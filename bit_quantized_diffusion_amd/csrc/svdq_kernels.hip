@@ -109,7 +109,14 @@ __global__ __launch_bounds__(256) void k1_quant_down_int4(
     float* __restrict__ lact, int ks) {
   constexpr int RANK = RT * 16;
   constexpr int TB = RT < 2 ? (RT > 0 ? RT : 1) : 2;    // L1 fragments per batch of loads (ranks of 16)
+  // ranks up to 64: the step's L1 slice [RANK][128 k] is loaded once per
+  // workgroup into a two-slot LDS ring and shared by the 4 waves (one
+  // barrier per step); larger ranks load their fragments per wave
+  constexpr bool L1S = RT > 0 && RT <= 4;
+  constexpr int kL1Row = 128 + 8;                       // bf16 elements per L1 row in LDS (16 bytes padding)
+  constexpr int kL1Chunks = L1S ? RANK * 16 / 256 : 1;  // 16-byte chunks per thread and step (1..4)
   extern __shared__ float lds_sinv[];                   // smooth_inv of this workgroup's K slice
+  __shared__ __attribute__((aligned(16))) uint16_t lds_l1[L1S ? 2 : 1][L1S ? RANK : 1][kL1Row];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int r16 = lane & 15;
@@ -137,6 +144,40 @@ __global__ __launch_bounds__(256) void k1_quant_down_int4(
   // whole, shorter-than-128 row, and then it is still inside the slice)
   auto sv = [&](int k) { return lds_sinv + (k - k_begin); };
 
+  // L1 slice of the step at kbase: chunk id = threadIdx.x + 256 i is row
+  // id/16, k kbase + 8 (id%16) (clamped into the row)
+  struct L1Regs {
+    uint4 v0, v1, v2, v3;
+  };
+  auto l1_chunk = [&](int kbase, int i) {
+    const int id = static_cast<int>(threadIdx.x) + 256 * i;
+    return *reinterpret_cast<const uint4*>(ldown + static_cast<size_t>(id >> 4) * K + min(kbase + 8 * (id & 15), K - 8));
+  };
+  auto l1_gload = [&](int kbase) {
+    L1Regs L;
+    L.v0 = l1_chunk(kbase, 0);
+    if constexpr (kL1Chunks > 1) L.v1 = l1_chunk(kbase, 1);
+    if constexpr (kL1Chunks > 2) L.v2 = l1_chunk(kbase, 2);
+    if constexpr (kL1Chunks > 3) L.v3 = l1_chunk(kbase, 3);
+    return L;
+  };
+  auto l1_put = [&](int slot, int i, const uint4& v) {
+    const int id = static_cast<int>(threadIdx.x) + 256 * i;
+    *reinterpret_cast<uint4*>(&lds_l1[slot][id >> 4][8 * (id & 15)]) = v;
+  };
+  auto l1_lstore = [&](int slot, L1Regs L) {
+    l1_put(slot, 0, L.v0);
+    if constexpr (kL1Chunks > 1) l1_put(slot, 1, L.v1);
+    if constexpr (kL1Chunks > 2) l1_put(slot, 2, L.v2);
+    if constexpr (kL1Chunks > 3) l1_put(slot, 3, L.v3);
+  };
+  L1Regs l1n;
+  if constexpr (L1S) {
+    l1n = l1_gload(k_begin);
+    l1_lstore(0, l1n);
+    __syncthreads();
+  }
+
   uint4 xn[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) xn[c] = *reinterpret_cast<const uint4*>(xr + kof(k_begin, c));
@@ -149,10 +190,21 @@ __global__ __launch_bounds__(256) void k1_quant_down_int4(
           dst[c][t] = *reinterpret_cast<const v4i*>(ldown + static_cast<size_t>((t0 + t) * 16 + r16) * K + kof(kbase, c));
   };
 
-  for (int kbase = k_begin; kbase < k_end; kbase += 128) {
+  int slot = 0;
+  for (int kbase = k_begin; kbase < k_end; kbase += 128, slot ^= 1) {
     uint4 xc[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) xc[c] = xn[c];
+    // L1 of this step (per wave) or of the next step (shared), issued
+    // before the next step's X so that waiting for them (in order) does not
+    // also wait for the X prefetch
+    v4i lb[4][TB];
+    const bool more = kbase + 128 < k_end;
+    if constexpr (L1S) {
+      if (more) l1n = l1_gload(kbase + 128);
+    } else if constexpr (RT > 0) {
+      load_l1(lb, kbase, 0);
+    }
     {
       const int nxt = kbase + 128 < k_end ? kbase + 128 : kbase;   // the last step re-reads itself (unused)
 #pragma unroll
@@ -168,10 +220,11 @@ __global__ __launch_bounds__(256) void k1_quant_down_int4(
       s0[c] = *reinterpret_cast<const float4*>(sv(k));
       s1[c] = *reinterpret_cast<const float4*>(sv(k) + 4);
     }
-    // first batch of L1 fragments, in flight during the quantization
-    v4i lb[4][TB];
-    if constexpr (RT > 0) load_l1(lb, kbase, 0);
 
+    // lanes past the slice's end compute on in-bounds data and zero it
+    // with a mask (a select would become a branch per element)
+    uint32_t vmask = valid ? 0xFFFFFFFFu : 0u;
+    asm volatile("" : "+v"(vmask));
     float xh[4][8];
     uint32_t pk[4][4];
 #pragma unroll
@@ -182,7 +235,7 @@ __global__ __launch_bounds__(256) void k1_quant_down_int4(
       for (int e = 0; e < 4; ++e) {
         const float lo = __uint_as_float(ws[e] << 16) * ss[2 * e];
         const float hi = __uint_as_float(ws[e] & 0xFFFF0000u) * ss[2 * e + 1];
-        const uint32_t p = valid ? cvt_pk_bf16(lo, hi) : 0u;
+        const uint32_t p = cvt_pk_bf16(lo, hi) & vmask;
         pk[c][e] = p;
         xh[c][2 * e] = __uint_as_float(p << 16);
         xh[c][2 * e + 1] = __uint_as_float(p & 0xFFFF0000u);
@@ -203,19 +256,30 @@ __global__ __launch_bounds__(256) void k1_quant_down_int4(
       const float inv = (s == 0.f) ? 0.f : __fdiv_rn(1.0f, s);
       // 8 codes per word: each code as the byte s000_0mmm (sign of a
       // negative code in bit 7, |q| in bits 0-2), E = the even-k bytes,
-      // O = the odd-k bytes, word = E | rotl32(O, 4)
+      // O = the odd-k bytes, word = E | rotl32(O, 4).  That byte is the FP8
+      // E4M3 image of q * 2^-9, so v_cvt_pk_fp8_f32 of fp32(x^ * inv) * 2^-9
+      // (exact: a power of two), clamped to +-7 * 2^-9 first, rounds to the
+      // nearest code with ties to the even one -- the rint of the rule.  A
+      // value that rounds to zero keeps no sign.
+      const float invs = inv * 0x1p-9f;
+      constexpr float kLim = 7.0f * 0x1p-9f;
+      auto unsign_zero = [](uint32_t w) {
+        const uint32_t mag = w & 0x07070707u;
+        return mag | (w & ((mag + 0x7F7F7F7Fu) & 0x80808080u));
+      };
       uint32_t word[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        uint32_t eo[2] = {0u, 0u};
+        float v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float qf = __builtin_rintf(xh[c][e] * inv);
-          qf = fminf(7.f, fmaxf(-7.f, qf));
-          const uint32_t b = static_cast<uint32_t>(static_cast<int>(fabsf(qf))) | (qf < 0.f ? 0x80u : 0u);
-          eo[e & 1] |= b << (8 * (e >> 1));
-        }
-        word[c] = eo[0] | __builtin_amdgcn_alignbit(eo[1], eo[1], 28);
+        for (int e = 0; e < 8; ++e) v[e] = fminf(kLim, fmaxf(-kLim, xh[c][e] * invs));
+        int ew = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[2], 0, false);
+        ew = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[6], ew, true);
+        int ow = __builtin_amdgcn_cvt_pk_fp8_f32(v[1], v[3], 0, false);
+        ow = __builtin_amdgcn_cvt_pk_fp8_f32(v[5], v[7], ow, true);
+        const uint32_t E = unsign_zero(static_cast<uint32_t>(ew));
+        const uint32_t O = unsign_zero(static_cast<uint32_t>(ow));
+        word[c] = E | __builtin_amdgcn_alignbit(O, O, 28);
       }
       // the lane's 32 codes are 16 contiguous bytes of the packed row
       if (row_ok && valid)
@@ -261,7 +325,21 @@ __global__ __launch_bounds__(256) void k1_quant_down_int4(
       }
     }
 
-    if constexpr (RT > 0) {
+    if constexpr (L1S) {
+      // fragments from the shared slice: L1 row t*16 + r16, k q*32 + c*8
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const v8bf a = __builtin_bit_cast(v8bf, (v4i{static_cast<int>(pk[c][0]), static_cast<int>(pk[c][1]),
+                                                     static_cast<int>(pk[c][2]), static_cast<int>(pk[c][3])}));
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          const v4i b = *reinterpret_cast<const v4i*>(&lds_l1[slot][t * 16 + r16][q * 32 + c * 8]);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, b), acc[t], 0, 0, 0);
+        }
+      }
+      if (more) l1_lstore(slot ^ 1, l1n);
+      __syncthreads();
+    } else if constexpr (RT > 0) {
 #pragma unroll
       for (int t0 = 0; t0 < RT; t0 += TB) {
         if (t0 > 0) load_l1(lb, kbase, t0);
