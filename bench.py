@@ -68,6 +68,7 @@ def parse():
     p.add_argument("--no-ablation", action="store_true",
                    help="skip the fused-vs-unfused (four kernel) comparison")
     p.add_argument("--no-mxfp4", action="store_true", help="skip the MXFP4 timing of the same layers")
+    p.add_argument("--no-mlp", action="store_true", help="skip the fused-MLP timing")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="time budget of the oracle sample (whole chunks of rows)")
     p.add_argument("--cpu-chunk", type=int, default=96, help="token rows per oracle chunk")
@@ -240,6 +241,10 @@ def main():
     if not args.no_ablation:
         ablation = fusion_ablation(bq, torch, np, sets, M, (s1, s2), per, stream, reps=10)
 
+    mlp = None
+    if not args.no_mlp:
+        mlp = mlp_fusion(bq, torch, np, sets, M, stream, reps=10)
+
     mx = None
     if not args.no_mxfp4:
         mx = mxfp4_layers(bq, torch, np, dev, (s1, s2), (lay1["w"], w2), (ax1, ax2),
@@ -262,6 +267,7 @@ def main():
         "cpu_baseline": cpu,
         "fusion_ablation": ablation,
         "mxfp4": mx,
+        "mlp_fusion": mlp,
     }
     print(json.dumps(out), flush=True)
 
@@ -308,6 +314,52 @@ def fusion_ablation(bq, torch, np, sets, M, specs, per, stream, reps):
                     "algorithmic_mb_unfused": round(unfused_b / 1e6, 1),
                     "mb_saved_by_fusion": round((unfused_b - fused_b) / 1e6, 1)}
     log(f"bench: fusion ablation {json.dumps(out)}")
+    return out
+
+
+def mlp_fusion(bq, torch, np, sets, M, stream, reps):
+    """The MLP pair fc2(GELU(fc1(x))) two ways, outside the timed step, on
+    the same buffers: GELU fused into fc1's GEMM epilogue with X2 written and
+    read back by fc2's first kernel (4 launches), and GELU plus fc2's first
+    kernel fused into fc1's GEMM epilogue (3 launches, no X2 in memory)."""
+    def gelu_path(b1, b2):
+        L1, L2 = b1["L"], b2["L"]
+        bq.quantize_act_lora_down(b1["x"], L1.smooth_inv, L1.lora_down, L1.rank, xq=b1["xq"], xs=b1["xs"],
+                                  lora_act=b1["la"])
+        bq.gemm_w4a4_lora_up_gelu(b1["xq"], b1["xs"], L1.wq, L1.ws, b1["la"], L1.lora_up, L1.bias, M, L1.N, L1.K,
+                                  L1.rank, y=b1["y"])
+        bq.quantize_act_lora_down(b1["y"], L2.smooth_inv, L2.lora_down, L2.rank, xq=b2["xq"], xs=b2["xs"],
+                                  lora_act=b2["la"])
+        bq.gemm_w4a4_lora_up(b2["xq"], b2["xs"], L2.wq, L2.ws, b2["la"], L2.lora_up, L2.bias, M, L2.N, L2.K,
+                             L2.rank, y=b2["y"])
+
+    def fused_path(b1, b2):
+        L1, L2 = b1["L"], b2["L"]
+        bq.quantize_act_lora_down(b1["x"], L1.smooth_inv, L1.lora_down, L1.rank, xq=b1["xq"], xs=b1["xs"],
+                                  lora_act=b1["la"])
+        bq.mlp_gemm_gelu_quant(b1["xq"], b1["xs"], L1.wq, L1.ws, b1["la"], L1.lora_up, L1.bias, M, L1.N, L1.K,
+                               L1.rank, L2.smooth_inv, L2.lora_down, L2.rank, xq2=b2["xq"], xs2=b2["xs"],
+                               lora_act2=b2["la"])
+        bq.gemm_w4a4_lora_up(b2["xq"], b2["xs"], L2.wq, L2.ws, b2["la"], L2.lora_up, L2.bias, M, L2.N, L2.K,
+                             L2.rank, y=b2["y"])
+
+    out = {}
+    for name, fn in (("gelu_in_fc1_epilogue_us", gelu_path), ("gelu_and_fc2_kernel1_in_fc1_epilogue_us", fused_path)):
+        for i in range(3):
+            fn(*sets[i % len(sets)])
+        torch.cuda.synchronize()
+        evs = []
+        for i in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn(*sets[i % len(sets)])
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        out[name] = round(1e3 * float(np.mean([a.elapsed_time(b) for a, b in evs])), 2)
+    out["speedup"] = round(out["gelu_in_fc1_epilogue_us"] / out["gelu_and_fc2_kernel1_in_fc1_epilogue_us"], 3)
+    out["note"] = "MLP pair fc1 4608x3072->12288, GELU(tanh), fc2 12288->3072, both rank 32, INT4"
+    log(f"bench: mlp fusion {json.dumps(out)}")
     return out
 
 

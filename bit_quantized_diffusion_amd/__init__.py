@@ -28,7 +28,7 @@ __all__ = [
     "INT4", "MXFP4", "SvdqError", "lib", "LIB_PATH", "status_string", "merge_lora",
     "version", "device_check", "packed_sizes", "act_sizes", "pack_weights",
     "quantize_act_lora_down", "gemm_w4a4_lora_up", "debug_group_partials", "unfused_linear",
-    "PackedLinear", "linear",
+    "PackedLinear", "linear", "gemm_w4a4_lora_up_gelu", "mlp_gemm_gelu_quant", "mlp",
 ]
 
 
@@ -199,6 +199,50 @@ def gemm_w4a4_lora_up(xq, xs, wq, ws, lora_act, lora_up, bias, M: int, N: int, K
     return y
 
 
+def gemm_w4a4_lora_up_gelu(xq, xs, wq, ws, lora_act, lora_up, bias, M: int, N: int, K: int, rank: int, y=None):
+    """Second fused kernel with the MLP's GELU fused: y = bf16(GELU(bf16(Y)))
+    (INT4).  Returns y bf16 [M][N]."""
+    torch = _torch()
+    dev = xq.device
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    check(lib.svdq_gemm_w4a4_lora_up_gelu(
+        _dptr(xq, torch.uint8, (M, K // 2), "xq"), _dptr(xs, torch.float16, (K // 64, M), "xs"),
+        _dptr(wq, torch.uint8, (N, K // 2), "wq"), _dptr(ws, torch.float16, (K // 64, N), "ws"),
+        _dptr(lora_act, torch.float32, (M, rank), "lora_act") if rank else None,
+        _dptr(lora_up, torch.bfloat16, (N, rank), "lora_up") if rank else None,
+        _dptr(bias, torch.bfloat16, (N,), "bias"),
+        _dptr(y, torch.bfloat16, (M, N), "y"),
+        M, N, K, rank, INT4, _stream(dev)))
+    return y
+
+
+def mlp_gemm_gelu_quant(xq, xs, wq, ws, lora_act, lora_up, bias, M: int, N: int, K: int, rank: int,
+                        smooth_inv2, lora_down2, rank2: int, xq2=None, xs2=None, lora_act2=None):
+    """First layer's second kernel fused with GELU and the second layer's
+    first kernel (INT4): returns (xq2 u8 [M][N/2], xs2 f16 [N/64][M],
+    lora_act2 f32 [M][rank2] or None)."""
+    torch = _torch()
+    dev = xq.device
+    if xq2 is None:
+        xq2 = torch.empty((M, N // 2), dtype=torch.uint8, device=dev)
+    if xs2 is None:
+        xs2 = torch.empty((N // 64, M), dtype=torch.float16, device=dev)
+    if rank2 and lora_act2 is None:
+        lora_act2 = torch.empty((M, rank2), dtype=torch.float32, device=dev)
+    check(lib.svdq_mlp_gemm_gelu_quant(
+        _dptr(xq, torch.uint8, (M, K // 2), "xq"), _dptr(xs, torch.float16, (K // 64, M), "xs"),
+        _dptr(wq, torch.uint8, (N, K // 2), "wq"), _dptr(ws, torch.float16, (K // 64, N), "ws"),
+        _dptr(lora_act, torch.float32, (M, rank), "lora_act") if rank else None,
+        _dptr(lora_up, torch.bfloat16, (N, rank), "lora_up") if rank else None,
+        _dptr(bias, torch.bfloat16, (N,), "bias"), M, N, K, rank,
+        _dptr(smooth_inv2, torch.float32, (N,), "smooth_inv2"),
+        _dptr(lora_down2, torch.bfloat16, (rank2, N), "lora_down2") if rank2 else None, rank2, INT4,
+        _dptr(xq2, torch.uint8, (M, N // 2), "xq2"), _dptr(xs2, torch.float16, (N // 64, M), "xs2"),
+        _dptr(lora_act2, torch.float32, (M, rank2), "lora_act2") if rank2 else None, _stream(dev)))
+    return xq2, xs2, (lora_act2 if rank2 else None)
+
+
 def unfused_linear(x, layer: "PackedLinear", y=None, xq=None, xs=None, lora_act=None):
     """The same layer as four separate kernels (quantize, down projection,
     4-bit GEMM, up projection): the baseline the two fusions are measured
@@ -276,6 +320,17 @@ class PackedLinear:
             ws=dev(packed["ws"], torch.float16 if precision == INT4 else torch.uint8),
             bias=None if bias_bf16 is None else dev(bias_bf16, torch.bfloat16),
         )
+
+
+def mlp(x, fc1: "PackedLinear", fc2: "PackedLinear", y=None):
+    """The MLP pair fc2(GELU(fc1(x))) with the activation and fc2's first
+    kernel fused into fc1's second kernel (INT4): three launches, no fc1
+    output in memory."""
+    M = x.shape[0]
+    xq, xs, la = quantize_act_lora_down(x, fc1.smooth_inv, fc1.lora_down, fc1.rank)
+    xq2, xs2, la2 = mlp_gemm_gelu_quant(xq, xs, fc1.wq, fc1.ws, la, fc1.lora_up, fc1.bias, M, fc1.N, fc1.K,
+                                        fc1.rank, fc2.smooth_inv, fc2.lora_down, fc2.rank)
+    return gemm_w4a4_lora_up(xq2, xs2, fc2.wq, fc2.ws, la2, fc2.lora_up, fc2.bias, M, fc2.N, fc2.K, fc2.rank, y=y)
 
 
 def linear(x, layer: PackedLinear, y=None):

@@ -26,6 +26,7 @@ EXPORTED = (
     "svdq_packed_sizes", "svdq_act_sizes", "svdq_pack_weights",
     "svdq_quantize_act_lora_down", "svdq_gemm_w4a4_lora_up",
     "svdq_unfused_linear", "svdq_debug_group_partials", "svdq_merge_lora",
+    "svdq_gemm_w4a4_lora_up_gelu", "svdq_mlp_gemm_gelu_quant",
 )
 
 
@@ -60,6 +61,8 @@ def _load():
         "svdq_unfused_linear": ([vp, i, i, vp, vp, i, vp, vp, vp, vp, i, i, vp, vp, vp, vp, vp], i),
         "svdq_debug_group_partials": ([vp, vp, i, i, i, i, i, i, i, vp, vp], i),
         "svdq_merge_lora": ([vp, vp, i, vp, vp, vp, i, i, i, vp, vp], i),
+        "svdq_gemm_w4a4_lora_up_gelu": ([vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp], i),
+        "svdq_mlp_gemm_gelu_quant": ([vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, vp, i, i, vp, vp, vp, vp], i),
     }
     for name, (args, ret) in sig.items():
         fn = getattr(lib, name)

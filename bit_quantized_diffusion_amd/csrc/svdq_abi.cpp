@@ -142,6 +142,50 @@ int svdq_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs, const uint8_t* wq,
                                                   precision, stream));
 }
 
+int svdq_gemm_w4a4_lora_up_gelu(const uint8_t* xq, const void* xs, const uint8_t* wq, const void* ws,
+                                const float* lora_act, const void* lora_up, const void* bias, void* y, int M, int N,
+                                int K, int rank, int precision, void* stream) {
+  int st = check_precision(precision);
+  if (st) return st;
+  if (precision != SVDQ_INT4) return SVDQ_ERR_INVALID_ARG;
+  if (!xq || !xs || !wq || !ws || !y) return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!lora_act || !lora_up)) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(wq) || !aligned16(ws) || !aligned16(y))
+    return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!aligned16(lora_act) || !aligned16(lora_up))) return SVDQ_ERR_INVALID_ARG;
+  if (bias && !aligned16(bias)) return SVDQ_ERR_INVALID_ARG;
+  if (M < 1 || N < 1) return SVDQ_ERR_SHAPE;
+  if ((st = check_k(K, precision))) return st;
+  if ((st = check_rank(rank, K, N))) return st;
+  if ((st = current_device_ok())) return st;
+  return hip_status(svdq_launch_gemm_int4_gelu(xq, xs, wq, ws, lora_act, lora_up, bias, y, M, N, K, rank, stream));
+}
+
+int svdq_mlp_gemm_gelu_quant(const uint8_t* xq, const void* xs, const uint8_t* wq, const void* ws,
+                             const float* lora_act, const void* lora_up, const void* bias, int M, int N, int K,
+                             int rank, const float* smooth_inv2, const void* lora_down2, int rank2, int precision,
+                             uint8_t* xq2, void* xs2, float* lora_act2, void* stream) {
+  int st = check_precision(precision);
+  if (st) return st;
+  if (precision != SVDQ_INT4) return SVDQ_ERR_INVALID_ARG;
+  if (!xq || !xs || !wq || !ws || !smooth_inv2 || !xq2 || !xs2) return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!lora_act || !lora_up)) return SVDQ_ERR_INVALID_ARG;
+  if (rank2 > 0 && (!lora_down2 || !lora_act2)) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(wq) || !aligned16(ws) || !aligned16(smooth_inv2) ||
+      !aligned16(xq2) || !aligned16(xs2))
+    return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!aligned16(lora_act) || !aligned16(lora_up))) return SVDQ_ERR_INVALID_ARG;
+  if (rank2 > 0 && (!aligned16(lora_down2) || !aligned16(lora_act2))) return SVDQ_ERR_INVALID_ARG;
+  if (bias && !aligned16(bias)) return SVDQ_ERR_INVALID_ARG;
+  if (M < 1 || N < 128 || N % 128 != 0) return SVDQ_ERR_SHAPE;
+  if ((st = check_k(K, precision))) return st;
+  if ((st = check_rank(rank, K, N))) return st;
+  if ((st = check_rank(rank2, N, N))) return st;
+  if ((st = current_device_ok())) return st;
+  return hip_status(svdq_launch_mlp_gemm_gelu_quant(xq, xs, wq, ws, lora_act, lora_up, bias, M, N, K, rank,
+                                                    smooth_inv2, lora_down2, rank2, xq2, xs2, lora_act2, stream));
+}
+
 int svdq_unfused_linear(const void* x, int M, int K, const float* smooth_inv, const void* lora_down, int rank,
                         const uint8_t* wq, const void* ws, const void* lora_up, const void* bias, int N,
                         int precision, uint8_t* xq, void* xs, float* lora_act, void* y, void* stream) {

@@ -43,6 +43,13 @@ int svdq_launch_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs,
                                   const void* bias, void* y, int M, int N,
                                   int K, int rank, int precision,
                                   void* stream);
+int svdq_launch_gemm_int4_gelu(const uint8_t* xq, const void* xs, const uint8_t* wq, const void* ws,
+                               const float* lora_act, const void* lora_up, const void* bias, void* y, int M, int N,
+                               int K, int rank, void* stream);
+int svdq_launch_mlp_gemm_gelu_quant(const uint8_t* xq, const void* xs, const uint8_t* wq, const void* ws,
+                                    const float* lora_act, const void* lora_up, const void* bias, int M, int N, int K,
+                                    int rank, const float* smooth_inv2, const void* lora_down2, int rank2,
+                                    uint8_t* xq2, void* xs2, float* lora_act2, void* stream);
 int svdq_launch_unfused_linear(const void* x, int M, int K,
                                const float* smooth_inv, const void* lora_down,
                                int rank, const uint8_t* wq, const void* ws,

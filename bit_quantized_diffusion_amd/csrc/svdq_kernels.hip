@@ -487,17 +487,139 @@ constexpr int kMxThreads = 256;
 constexpr int kMxYRow = kTile + 8;               // staging row stride of the output tile (bf16 elements)
 static_assert(2 * kMxSlot >= kTile * kMxYRow * 2, "output staging fits in the ring");
 
+// tanh-form GELU, 0.5 y (1 + tanh(u)) with u = sqrt(2/pi) (y + 0.044715 y^3),
+// evaluated as y / (1 + exp(-2u)) with the hardware exp2 and reciprocal
+// (relative error a few ulp of fp32).
+__device__ __forceinline__ float gelu_tanh_f32(float y) {
+  const float u = 0.7978845608028654f * __builtin_fmaf(0.044715f * y, y * y, y);
+  const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * u);     // exp(-2u)
+  return y * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Second layer of an MLP pair, fed by the first layer's epilogue: its
+// smoothing, L1 (lora_down2 [rank2][N]) and kernel-1 outputs.
+struct MlpOut {
+  const float* sinv2;
+  const uint16_t* ldown2;
+  int rank2;
+  uint8_t* xq2;
+  uint16_t* xs2;
+  float* lact2;
+};
+
+// The second layer's kernel 1 on a staged 128 x 128 tile of X2 (bf16,
+// [m][n] with row stride kMxYRow); N % 128 == 0.
+__device__ __forceinline__ void mlp_tail(uint16_t* __restrict__ stg, int M, int N, int n0, int m0, int tid,
+                                         const MlpOut& mo) {
+  // thread t owns one 64-column group of one tile row: row t/2, columns
+  // 64 (t%2) .. +64, so the group's absmax and scale stay in its registers
+  const int r = tid >> 1, c0 = (tid & 1) * 64;
+  const int m = m0 + r;
+  const size_t rowb2 = static_cast<size_t>(N / 2);
+  constexpr float kLim = 7.0f * 0x1p-9f;
+  auto unsign_zero = [](uint32_t w) {
+    const uint32_t mag = w & 0x07070707u;
+    return mag | (w & ((mag + 0x7F7F7F7Fu) & 0x80808080u));
+  };
+  uint16_t* srow = stg + r * kMxYRow + c0;
+  float xh[64];
+  float amax = 0.f;
+#pragma unroll
+  for (int ch = 0; ch < 8; ++ch) {
+    const uint4 v = *reinterpret_cast<const uint4*>(srow + 8 * ch);
+    const float4 sa = *reinterpret_cast<const float4*>(mo.sinv2 + n0 + c0 + 8 * ch);
+    const float4 sb = *reinterpret_cast<const float4*>(mo.sinv2 + n0 + c0 + 8 * ch + 4);
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    const float sv[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+    uint32_t p[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p[e] = cvt_pk_bf16(__uint_as_float(w4[e] << 16) * sv[2 * e], __uint_as_float(w4[e] & 0xFFFF0000u) * sv[2 * e + 1]);
+      xh[8 * ch + 2 * e] = __uint_as_float(p[e] << 16);
+      xh[8 * ch + 2 * e + 1] = __uint_as_float(p[e] & 0xFFFF0000u);
+      amax = fmaxf(amax, fmaxf(fabsf(xh[8 * ch + 2 * e]), fabsf(xh[8 * ch + 2 * e + 1])));
+    }
+    *reinterpret_cast<uint4*>(srow + 8 * ch) = make_uint4(p[0], p[1], p[2], p[3]);   // x^2 for the MFMA
+  }
+  const uint32_t sbits = f16_sat_bits(__fdiv_rn(amax, 7.0f));
+  const float sc = f16_bits_to_f32(sbits);
+  const float invs = ((sc == 0.f) ? 0.f : __fdiv_rn(1.0f, sc)) * 0x1p-9f;
+  uint32_t words[8];
+#pragma unroll
+  for (int ch = 0; ch < 8; ++ch) {
+    float qv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[e] = fminf(kLim, fmaxf(-kLim, xh[8 * ch + e] * invs));
+    int ew = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[2], 0, false);
+    ew = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4], qv[6], ew, true);
+    int ow = __builtin_amdgcn_cvt_pk_fp8_f32(qv[1], qv[3], 0, false);
+    ow = __builtin_amdgcn_cvt_pk_fp8_f32(qv[5], qv[7], ow, true);
+    const uint32_t E = unsign_zero(static_cast<uint32_t>(ew));
+    const uint32_t O = unsign_zero(static_cast<uint32_t>(ow));
+    words[ch] = E | __builtin_amdgcn_alignbit(O, O, 28);
+  }
+  if (m < M) {
+    uint4* dst = reinterpret_cast<uint4*>(mo.xq2 + static_cast<size_t>(m) * rowb2 + (n0 + c0) / 2);
+    dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
+    dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
+    mo.xs2[static_cast<size_t>((n0 + c0) / 64) * M + m] = static_cast<uint16_t>(sbits);
+  }
+  __syncthreads();
+  // partial down projection over the tile's 128 columns: wave w, rows
+  // 32w .. +32 (two 16-row MFMA tiles), 16 ranks per MFMA, K = 128 in 4
+  // steps of 32; lane (r16, q) holds row r16, columns 32s + 8q .. +8
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, qq = lane >> 4;
+  for (int rt = 0; rt < mo.rank2 / 16; ++rt) {
+    v4f d[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const v4i b = *reinterpret_cast<const v4i*>(mo.ldown2 + static_cast<size_t>(rt * 16 + r16) * N + n0 + 32 * ks + 8 * qq);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const v4i a = *reinterpret_cast<const v4i*>(stg + (32 * wave + 16 * mt + r16) * kMxYRow + 32 * ks + 8 * qq);
+        d[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), d[mt],
+                                                       0, 0, 0);
+      }
+    }
+    float dv[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dv[mt][i] = d[mt][i];
+        asm volatile("" : "+v"(dv[mt][i]));     // read the MFMA results before the predicated atomics
+      }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 32 * wave + 16 * mt + 4 * qq + i;
+        if (m < M) atomicAdd(mo.lact2 + static_cast<size_t>(m) * mo.rank2 + rt * 16 + r16, dv[mt][i]);
+      }
+  }
+}
+
 // Shared epilogue of the 128 x 128 GEMM tiles (4 waves of 64 x 64, Y^T
 // MFMA layout): acc += bf16(lora_act) . L2 on the accumulators (16 ranks per
 // v_mfma_f32_32x32x16_bf16), the bias, one rounding to bf16, then the tile
 // goes through LDS (stg: kTile rows of kMxYRow bf16) so that each store
 // writes 16 contiguous bytes and eight lanes fill a 128-byte segment of a Y
 // row.  Every wave must be past its last LDS read of the main loop.
+//
+// EPI = 0 writes Y.  EPI = 1 writes bf16(GELU(Y)) (Y rounded to bf16 first,
+// as the next layer would read it).  EPI = 2 writes nothing of Y: the tile
+// of X2 = bf16(GELU(Y)) becomes the second layer's kernel-1 input --
+// x^2 = bf16(X2 * smooth_inv2), its 4-bit codes and fp16 scales per 64
+// columns (tile-local: a group lies inside the 128-column tile), and its
+// partial down projection x^2 . L1_2 over the tile's 128 columns, summed
+// into lact2 with fp32 atomics (lact2 cleared beforehand).
+template <int EPI>
 __device__ __forceinline__ void epilogue_tile128(v16f (&acc)[2][2], uint16_t* __restrict__ stg,
                                                  const float* __restrict__ lact, const uint16_t* __restrict__ lup,
                                                  const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M,
                                                  int N, int rank, int n0, int m0, int wn, int wm, int l32, int h,
-                                                 int tid) {
+                                                 int tid, const MlpOut& mo) {
   for (int c0 = 0; c0 < rank; c0 += 16) {
     const int j = c0 + 8 * h;
     v4i ub[2], ua[2];
@@ -558,13 +680,20 @@ __device__ __forceinline__ void epilogue_tile128(v16f (&acc)[2][2], uint16_t* __
       for (int j = 0; j < 4; ++j) {
         const int ml = wm * 64 + jt * 32 + l32;
         const int nl = wn * 64 + it * 32 + 8 * j + 4 * h;
-        const uint32_t h0 = bf16_rne_bits(acc[it][jt][4 * j + 0] + bv[it][j][0]);
-        const uint32_t h1 = bf16_rne_bits(acc[it][jt][4 * j + 1] + bv[it][j][1]);
-        const uint32_t h2 = bf16_rne_bits(acc[it][jt][4 * j + 2] + bv[it][j][2]);
-        const uint32_t h3 = bf16_rne_bits(acc[it][jt][4 * j + 3] + bv[it][j][3]);
-        *reinterpret_cast<uint2*>(stg + ml * kMxYRow + nl) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+        uint32_t hv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          hv[i] = bf16_rne_bits(acc[it][jt][4 * j + i] + bv[it][j][i]);
+          if constexpr (EPI >= 1) hv[i] = bf16_rne_bits(gelu_tanh_f32(__uint_as_float(hv[i] << 16)));
+        }
+        *reinterpret_cast<uint2*>(stg + ml * kMxYRow + nl) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
       }
   __syncthreads();
+
+  if constexpr (EPI == 2) {
+    mlp_tail(stg, M, N, n0, m0, tid, mo);
+    return;
+  }
 
   // 16-byte stores: thread t writes channels 8(t%16) .. +7 of tile rows t/16 + 16i
   const int c8 = (tid & 15) * 8;
@@ -739,8 +868,8 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_mxfp4(
     if (st + 1 < S) iteration(st + 1, Slot<1>{});
   }
 
-  epilogue_tile128(acc, reinterpret_cast<uint16_t*>(&lds_c[0][0]), lact, lup, bias, y, M, N, rank, n0, m0, wn, wm,
-                   l32, h, tid);
+  epilogue_tile128<0>(acc, reinterpret_cast<uint16_t*>(&lds_c[0][0]), lact, lup, bias, y, M, N, rank, n0, m0, wn,
+                      wm, l32, h, tid, MlpOut{});
 }
 
 // ---------------------------------------------------------------------------
@@ -766,13 +895,13 @@ constexpr int kI4Row = 2 * 64 + 16;           // LDS row stride: 128 FP8 codes +
 constexpr int kI4Slot = 2 * kTile * kI4Row;   // W rows, then X rows
 static_assert(2 * kI4Slot >= kTile * kMxYRow * 2, "output staging fits in the ring");
 
-template <bool DEBUG>
+template <bool DEBUG, int EPI = 0>
 __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
     const uint8_t* __restrict__ xq, const uint16_t* __restrict__ xs,
     const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
     const float* __restrict__ lact, const uint16_t* __restrict__ lup,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N, int K, int rank,
-    int win_m0, int win_n0, int win_mt, int win_nt, int32_t* __restrict__ dbg) {
+    int win_m0, int win_n0, int win_mt, int win_nt, int32_t* __restrict__ dbg, MlpOut mo) {
   __shared__ __attribute__((aligned(16))) int8_t lds_c[2][kI4Slot];
   // per slot, operand (0 = W, 1 = X), group of the stage and row: the E8M0
   // exponent byte of the scale and its fp16 significand
@@ -980,8 +1109,8 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   }
 
   if constexpr (!DEBUG)
-    epilogue_tile128(acc, reinterpret_cast<uint16_t*>(&lds_c[0][0]), lact, lup, bias, y, M, N, rank, n0, m0, wn, wm,
-                     l32, h, tid);
+    epilogue_tile128<EPI>(acc, reinterpret_cast<uint16_t*>(&lds_c[0][0]), lact, lup, bias, y, M, N, rank, n0, m0, wn,
+                          wm, l32, h, tid, mo);
 }
 
 // K1 grid: 64-row blocks x K slices.  The slice count is chosen so that
@@ -1099,7 +1228,7 @@ hipError_t launch_unfused(const void* x, int M, int K, const float* sinv, const 
   const int tiles = ((N + kTile - 1) / kTile) * ((M + kTile - 1) / kTile);               // 3: 4-bit GEMM
   hipLaunchKernelGGL(k2_gemm_int4<false>, dim3(tiles), dim3(kMxThreads), 0, st, xq, static_cast<const uint16_t*>(xs),
                      wq, static_cast<const uint16_t*>(ws), nullptr, nullptr, nullptr, static_cast<uint16_t*>(y), M, N,
-                     K, 0, 0, 0, 0, 0, nullptr);
+                     K, 0, 0, 0, 0, 0, nullptr, MlpOut{});
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_up_proj, dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, st, lact,  // 4: up projection
                      static_cast<const uint16_t*>(lup), static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y),
@@ -1147,7 +1276,38 @@ extern "C" int svdq_launch_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs, 
   hipLaunchKernelGGL(k2_gemm_int4<false>, dim3(tiles), dim3(kMxThreads), 0, static_cast<hipStream_t>(stream), xq,
                      static_cast<const uint16_t*>(xs), wq, static_cast<const uint16_t*>(ws), lora_act,
                      static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias),
-                     static_cast<uint16_t*>(y), M, N, K, rank, 0, 0, 0, 0, nullptr);
+                     static_cast<uint16_t*>(y), M, N, K, rank, 0, 0, 0, 0, nullptr, MlpOut{});
+  return static_cast<int>(hipGetLastError());
+}
+
+extern "C" int svdq_launch_gemm_int4_gelu(const uint8_t* xq, const void* xs, const uint8_t* wq, const void* ws,
+                                          const float* lora_act, const void* lora_up, const void* bias, void* y, int M,
+                                          int N, int K, int rank, void* stream) {
+  const int tiles = ((N + kTile - 1) / kTile) * ((M + kTile - 1) / kTile);
+  hipLaunchKernelGGL((k2_gemm_int4<false, 1>), dim3(tiles), dim3(kMxThreads), 0, static_cast<hipStream_t>(stream), xq,
+                     static_cast<const uint16_t*>(xs), wq, static_cast<const uint16_t*>(ws), lora_act,
+                     static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias),
+                     static_cast<uint16_t*>(y), M, N, K, rank, 0, 0, 0, 0, nullptr, MlpOut{});
+  return static_cast<int>(hipGetLastError());
+}
+
+extern "C" int svdq_launch_mlp_gemm_gelu_quant(const uint8_t* xq, const void* xs, const uint8_t* wq, const void* ws,
+                                               const float* lora_act, const void* lora_up, const void* bias, int M,
+                                               int N, int K, int rank, const float* smooth_inv2,
+                                               const void* lora_down2, int rank2, uint8_t* xq2, void* xs2,
+                                               float* lora_act2, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (rank2 > 0) {
+    const size_t n = static_cast<size_t>(M) * rank2;
+    hipLaunchKernelGGL(fill_zero_f32, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, lora_act2, n);
+  }
+  const int tiles = ((N + kTile - 1) / kTile) * ((M + kTile - 1) / kTile);
+  const MlpOut mo{smooth_inv2, static_cast<const uint16_t*>(lora_down2), rank2, xq2, static_cast<uint16_t*>(xs2),
+                  lora_act2};
+  hipLaunchKernelGGL((k2_gemm_int4<false, 2>), dim3(tiles), dim3(kMxThreads), 0, st, xq,
+                     static_cast<const uint16_t*>(xs), wq, static_cast<const uint16_t*>(ws), lora_act,
+                     static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias), nullptr, M, N, K, rank,
+                     0, 0, 0, 0, nullptr, mo);
   return static_cast<int>(hipGetLastError());
 }
 
@@ -1177,6 +1337,6 @@ extern "C" int svdq_launch_debug_group_partials(const uint8_t* xq, const uint8_t
                                                 int n0, int mt, int nt, int32_t* out, void* stream) {
   const int tiles = ((nt + kTile - 1) / kTile) * ((mt + kTile - 1) / kTile);
   hipLaunchKernelGGL(k2_gemm_int4<true>, dim3(tiles), dim3(kMxThreads), 0, static_cast<hipStream_t>(stream), xq,
-                     nullptr, wq, nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, 0, m0, n0, mt, nt, out);
+                     nullptr, wq, nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, 0, m0, n0, mt, nt, out, MlpOut{});
   return static_cast<int>(hipGetLastError());
 }

@@ -197,6 +197,43 @@ SVDQ_API int svdq_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs,
                            int M, int N, int K, int rank, int precision,
                            void* stream);
 
+/* First layer of an MLP pair with its activation fused: the original
+ * engine's model-specific paths include a fused GELU/MLP kernel (blog
+ * "Nunchaku 4-bit inference in Diffusers", "Introducing Nunchaku Lite").
+ * The activation is the tanh-form GELU of FLUX's MLP (a reading; the pages
+ * do not name the form).  INT4 only.
+ *
+ * svdq_gemm_w4a4_lora_up_gelu: as svdq_gemm_w4a4_lora_up, but y receives
+ * bf16(GELU(Y)) with Y the layer's bf16 output (rounded first, as the next
+ * layer would read it) and GELU(y) = 0.5 y (1 + tanh(sqrt(2/pi) (y +
+ * 0.044715 y^3))) evaluated in fp32.
+ *
+ * svdq_mlp_gemm_gelu_quant: writes no Y at all.  The tile of X2 =
+ * bf16(GELU(Y)) goes straight into the second layer's first kernel
+ * (svdq_quantize_act_lora_down's rule with smooth_inv2 and lora_down2):
+ *   smooth_inv2 (dev) [N] fp32            second layer's smoothing
+ *   lora_down2  (dev) [rank2][N] bf16     second layer's L1^T; ignored if rank2 == 0
+ *   xq2         (dev) [M][N/2] uint8      out, 4-bit codes of X2^
+ *   xs2         (dev) [N/64][M] fp16      out
+ *   lora_act2   (dev) [M][rank2] fp32     out (cleared, then summed over the
+ *                                         output tiles with fp32 atomics)
+ * N % 128 == 0 (a 64-column group lies inside one 128-column tile), else
+ * SVDQ_ERR_SHAPE; rank2 follows the rank rule with K = N.  Other arguments
+ * as for svdq_gemm_w4a4_lora_up. */
+SVDQ_API int svdq_gemm_w4a4_lora_up_gelu(const uint8_t* xq, const void* xs,
+                           const uint8_t* wq, const void* ws,
+                           const float* lora_act, const void* lora_up,
+                           const void* bias, void* y,
+                           int M, int N, int K, int rank, int precision,
+                           void* stream);
+SVDQ_API int svdq_mlp_gemm_gelu_quant(const uint8_t* xq, const void* xs,
+                           const uint8_t* wq, const void* ws,
+                           const float* lora_act, const void* lora_up,
+                           const void* bias, int M, int N, int K, int rank,
+                           const float* smooth_inv2, const void* lora_down2, int rank2,
+                           int precision, uint8_t* xq2, void* xs2, float* lora_act2,
+                           void* stream);
+
 /* Unfused baseline of the same layer, for measuring what the two fusions
  * save (model card "svdq-int4-flux.1-dev", Nunchaku engine caption (a): a
  * naive low-rank branch as separate kernels costs an extra 16-bit read of

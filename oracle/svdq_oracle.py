@@ -354,9 +354,15 @@ def merge_lora(l1_bits, l2_bits, smooth_inv, a_bits, b_bits):
 # ---------------------------------------------------------------------------
 
 def gelu_tanh(y):
-    """tanh-approximated GELU in fp64 (FLUX's MLP activation)."""
+    """tanh-approximated GELU in fp64 (FLUX's MLP activation):
+    0.5 y (1 + tanh(u)), u = sqrt(2/pi) (y + 0.044715 y^3).  Evaluated as
+    y / (1 + exp(-2u)), the same function, so that negative y do not lose
+    everything to the cancellation in 1 + tanh(u) (which is 0 in fp64 once
+    u < -19); exp overflowing to inf gives -0 for very negative y."""
     y = np.asarray(y, dtype=np.float64)
-    return 0.5 * y * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (y + 0.044715 * y ** 3)))
+    u = np.sqrt(2.0 / np.pi) * (y + 0.044715 * y ** 3)
+    with np.errstate(over="ignore"):
+        return y / (1.0 + np.exp(-2.0 * u))
 
 
 def reference_linear(x_bits, w_bits, bias_bits=None) -> np.ndarray:

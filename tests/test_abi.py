@@ -104,6 +104,31 @@ def test_hot_calls_reject_bad_shapes():
     assert L.svdq_debug_group_partials(FAKE, FAKE, 16, 16, 64, 10, 0, 7, 1, FAKE, None) == bq.SVDQ_ERR_SHAPE
 
 
+def test_mlp_calls_validate():
+    """The GELU and fused-MLP calls: NULL / misaligned pointers, MXFP4
+    (INT4 only), N not a multiple of 128 for the fused pair, rank rules."""
+    L = bq.lib
+    g = L.svdq_gemm_w4a4_lora_up_gelu
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 16, 16, 64, 16, 0, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, MIS, FAKE, 16, 16, 64, 16, 0, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 16, 16, 128, 16, bq.MXFP4, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 16, 16, 96, 16, 0, None) == bq.SVDQ_ERR_SHAPE
+    f = L.svdq_mlp_gemm_gelu_quant
+    ok = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 16, 256, 64, 16, FAKE, FAKE, 16, 0, FAKE, FAKE, FAKE, None)
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a11=None) == bq.SVDQ_ERR_INVALID_ARG          # smooth_inv2
+    assert call(a12=None) == bq.SVDQ_ERR_INVALID_ARG          # lora_down2 with rank2 > 0
+    assert call(a15=MIS) == bq.SVDQ_ERR_INVALID_ARG           # xq2
+    assert call(a14=bq.MXFP4) == bq.SVDQ_ERR_INVALID_ARG
+    assert call(a8=192) == bq.SVDQ_ERR_SHAPE                  # N % 128 != 0
+    assert call(a13=24) == bq.SVDQ_ERR_SHAPE                  # rank2 not a multiple of 16
+    assert call(a12=None, a13=0, a17=None) != bq.SVDQ_ERR_INVALID_ARG   # rank2 == 0 needs no L1 / lora_act2
+
+
 @pytest.mark.skipif(_gpu_present(), reason="checks the no-device path")
 def test_no_device_gives_unsupported_device_not_a_crash():
     L = bq.lib

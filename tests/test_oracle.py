@@ -442,3 +442,26 @@ def test_mx_power_of_two_grid_lossless():
         codes, sb = O.mx_quantize_blocks(vals.astype(np.float32))
         assert np.all(sb == e + 127)
         assert np.array_equal(O.mx_decode(codes, sb), vals)
+
+
+# ---------------------------------------------------------------------------
+# GELU of the MLP pair
+# ---------------------------------------------------------------------------
+
+def test_gelu_tanh_form():
+    """The logistic evaluation is the tanh form: against math.tanh where the
+    tanh form has no cancellation, odd part y, limits, and the tail that the
+    tanh form loses to cancellation."""
+    import math
+    ys = np.linspace(-6.0, 8.0, 561)
+    want = [0.5 * y * (1.0 + math.tanh(math.sqrt(2.0 / math.pi) * (y + 0.044715 * y ** 3))) for y in ys]
+    got = O.gelu_tanh(ys)
+    big = np.abs(ys) < 3.0
+    assert np.allclose(got[big], np.array(want)[big], rtol=1e-13, atol=1e-15)
+    # gelu(y) - gelu(-y) = y (the odd part of 0.5 y tanh(u) vanishes)
+    assert np.allclose(O.gelu_tanh(ys) - O.gelu_tanh(-ys), ys, rtol=1e-13, atol=1e-13)
+    assert O.gelu_tanh(np.array([0.0]))[0] == 0.0
+    assert O.gelu_tanh(np.array([50.0]))[0] == 50.0
+    t = O.gelu_tanh(np.array([-10.0, -1e4]))
+    assert t[0] < 0 and t[0] > -1e-30          # tiny, not rounded to 0 by cancellation
+    assert t[1] == 0.0 and np.signbit(t[1])    # exp overflow: -0
