@@ -20,7 +20,9 @@ dense 8-bit matrix-core peak (int8 and fp8 run at the same rate).
 
 The `mxfp4` object times the same two layers packed in MXFP4 (E2M1 codes,
 E8M0 scales per 32 k) outside the timed step, against the dense FP4
-matrix-core peak.
+matrix-core peak.  The `w4a16` object times the same weights as a 4-bit
+weight-only layer (bf16 activations, one kernel) against the dense bf16
+matrix-core peak, the comparison the pages quote W4A4 speedups against.
 
 `--calibrate-copy` instead runs a plain elementwise copy of 1 GiB a few
 times; its FETCH_SIZE / WRITE_SIZE counters give the factor that turns the
@@ -42,6 +44,7 @@ sys.path.insert(0, ROOT)
 METRIC = ("fused W4A4+LoRA-r32 linear: µs/layer, TOPS & % INT8-MFMA roofline (FLUX MLP)")
 INT8_PEAK_TOPS = 5033.0        # 256 CU x 2.4 GHz x 8192 int8/fp8 ops/clk/CU (dense)
 FP4_PEAK_TOPS = 10066.0        # 256 CU x 2.4 GHz x 16384 fp4 ops/clk/CU (dense)
+BF16_PEAK_TFLOPS = 2517.0      # 256 CU x 2.4 GHz x 4096 bf16 flops/clk/CU (dense)
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "bit_quantized_diffusion_amd", "csrc", "svdq_kernels.hip")
 TRAFFIC = os.path.join(ROOT, "profiles", "k2_gemm_int4_flux_mlp_hbm_traffic.md")
@@ -69,6 +72,8 @@ def parse():
                    help="skip the fused-vs-unfused (four kernel) comparison")
     p.add_argument("--no-mxfp4", action="store_true", help="skip the MXFP4 timing of the same layers")
     p.add_argument("--no-mlp", action="store_true", help="skip the fused-MLP timing")
+    p.add_argument("--no-w4a16", action="store_true",
+                   help="skip the W4A16 (4-bit weight, bf16 activation) comparison timing")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="time budget of the oracle sample (whole chunks of rows)")
     p.add_argument("--cpu-chunk", type=int, default=96, help="token rows per oracle chunk")
@@ -250,6 +255,11 @@ def main():
         mx = mxfp4_layers(bq, torch, np, dev, (s1, s2), (lay1["w"], w2), (ax1, ax2),
                           (lay1["bias"], synth.gen_bias(s2)), (x1, x2), args.sets, stream, reps=20)
 
+    w16 = None
+    if not args.no_w4a16:
+        w16 = w4a16_layers(bq, torch, np, dev, (s1, s2), (lay1["w"], w2), (lay1["bias"], synth.gen_bias(s2)),
+                           (x1, x2), args.sets, stream, per, reps=20)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(lay1, pk1, s1, args.cpu_seconds, args.cpu_chunk)
@@ -268,6 +278,7 @@ def main():
         "fusion_ablation": ablation,
         "mxfp4": mx,
         "mlp_fusion": mlp,
+        "w4a16": w16,
     }
     print(json.dumps(out), flush=True)
 
@@ -417,6 +428,65 @@ def mxfp4_layers(bq, torch, np, dev, specs, ws, axs, biases, xs, n_sets, stream,
                        "avg_launch_us": round(k2_us, 2),
                        "peak_basis": "dense fp4 matrix-core rate, 256 CU x 2.4 GHz x 16384 ops/clk"}
     log(f"bench: mxfp4 {json.dumps(out)}")
+    return out
+
+
+def w4a16_layers(bq, torch, np, dev, specs, ws, biases, xs, n_sets, stream, per, reps):
+    """The same fc1 / fc2 weights as W4A16 (INT4 codes, fp16 scales per 64 k,
+    bf16 activations, no smoothing or low-rank branch): one kernel per layer,
+    timed per launch with HIP events on the library's stream over rotated
+    buffer sets, outside the timed step.  `w4a4_speedup` = W4A16 time over
+    the fused W4A4 layer's time (both kernels) from the timed step.  A plain
+    bf16 torch.matmul of the unquantized weights is timed beside it for
+    context."""
+    out = {}
+    k_all = []
+    for tag, s, w, bias, x in zip(("fc1", "fc2"), specs, ws, biases, xs):
+        wq, wsc = bq.pack_w4a16(w)
+        b = torch.from_numpy(np.ascontiguousarray(bias).view(np.int16)).view(torch.bfloat16).to(dev)
+        wd = torch.from_numpy(np.ascontiguousarray(w).view(np.int16)).view(torch.bfloat16).to(dev)
+        sets = []
+        for _ in range(n_sets):
+            sets.append(dict(x=x.clone(), wq=torch.from_numpy(wq).to(dev), ws=torch.from_numpy(wsc).to(dev),
+                             w=wd.clone(), y=torch.empty((s.M, s.N), dtype=torch.bfloat16, device=dev)))
+        del wd
+
+        def run(bset, kind):
+            if kind == "w4a16":
+                bq.gemm_w4a16(bset["x"], bset["wq"], bset["ws"], b, s.N, y=bset["y"])
+            else:
+                torch.addmm(b, bset["x"], bset["w"].t(), out=bset["y"])
+
+        res = {}
+        for kind in ("w4a16", "bf16"):
+            for i in range(3):
+                run(sets[i % n_sets], kind)
+            torch.cuda.synchronize()
+            evs = []
+            for i in range(reps):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                e[0].record(stream)
+                run(sets[i % n_sets], kind)
+                e[1].record(stream)
+                evs.append(e)
+            torch.cuda.synchronize()
+            res[kind] = [e[0].elapsed_time(e[1]) for e in evs]
+        k_all += res["w4a16"]
+        us = 1e3 * float(np.mean(res["w4a16"]))
+        us_bf16 = 1e3 * float(np.mean(res["bf16"]))
+        ops = 2.0 * s.M * s.N * s.K
+        out[tag] = {"us_layer": round(us, 2), "tops": round(ops / (us * 1e-6) / 1e12, 1),
+                    "w4a4_speedup": round(us / per[tag]["us_layer"], 3),
+                    "us_bf16_torch_matmul": round(us_bf16, 2)}
+        del sets
+    us = 1e3 * float(np.mean(k_all))
+    ops = 2.0 * specs[0].M * specs[0].N * specs[0].K
+    achieved = ops / (us * 1e-6) / 1e12
+    out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                       "kernel": "k2_gemm_w4a16 (fc1 and fc2)", "avg_launch_us": round(us, 2),
+                       "peak_basis": "dense bf16 matrix-core rate, 256 CU x 2.4 GHz x 4096 flops/clk"}
+    log(f"bench: w4a16 {json.dumps(out)}")
     return out
 
 

@@ -29,6 +29,7 @@ __all__ = [
     "version", "device_check", "packed_sizes", "act_sizes", "pack_weights",
     "quantize_act_lora_down", "gemm_w4a4_lora_up", "debug_group_partials", "unfused_linear",
     "PackedLinear", "linear", "gemm_w4a4_lora_up_gelu", "mlp_gemm_gelu_quant", "mlp",
+    "pack_w4a16", "gemm_w4a16",
 ]
 
 
@@ -241,6 +242,30 @@ def mlp_gemm_gelu_quant(xq, xs, wq, ws, lora_act, lora_up, bias, M: int, N: int,
         _dptr(xq2, torch.uint8, (M, N // 2), "xq2"), _dptr(xs2, torch.float16, (N // 64, M), "xs2"),
         _dptr(lora_act2, torch.float32, (M, rank2), "lora_act2") if rank2 else None, _stream(dev)))
     return xq2, xs2, (lora_act2 if rank2 else None)
+
+
+def pack_w4a16(w_bf16: np.ndarray):
+    """W4A16 comparison weights on the CPU: w_bf16 uint16 bf16 bits [N][K] ->
+    (wq uint8 [N][K/2], ws float16 [K/64][N])."""
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    N, K = w.shape
+    wq = np.empty((N, K // 2), np.uint8)
+    ws = np.empty((K // 64, N), np.float16)
+    check(lib.svdq_pack_w4a16(_np_ptr(w), K, N, _np_ptr(wq), _np_ptr(ws)))
+    return wq, ws
+
+
+def gemm_w4a16(x, wq, ws, bias, N: int, y=None):
+    """W4A16 comparison GEMM: y = bf16(x . dequant(W)^T + bias), x bf16 [M][K]."""
+    torch = _torch()
+    M, K = x.shape
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    check(lib.svdq_gemm_w4a16(
+        _dptr(x, torch.bfloat16, (M, K), "x"), _dptr(wq, torch.uint8, (N, K // 2), "wq"),
+        _dptr(ws, torch.float16, (K // 64, N), "ws"), _dptr(bias, torch.bfloat16, (N,), "bias"),
+        _dptr(y, torch.bfloat16, (M, N), "y"), M, N, K, _stream(x.device)))
+    return y
 
 
 def unfused_linear(x, layer: "PackedLinear", y=None, xq=None, xs=None, lora_act=None):

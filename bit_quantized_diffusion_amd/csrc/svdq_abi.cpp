@@ -186,6 +186,18 @@ int svdq_mlp_gemm_gelu_quant(const uint8_t* xq, const void* xs, const uint8_t* w
                                                     smooth_inv2, lora_down2, rank2, xq2, xs2, lora_act2, stream));
 }
 
+int svdq_gemm_w4a16(const void* x, const uint8_t* wq, const void* ws, const void* bias, void* y, int M, int N,
+                    int K, void* stream) {
+  if (!x || !wq || !ws || !y) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(ws) || !aligned16(y)) return SVDQ_ERR_INVALID_ARG;
+  if (bias && !aligned16(bias)) return SVDQ_ERR_INVALID_ARG;
+  if (M < 1 || N < 1) return SVDQ_ERR_SHAPE;
+  int st;
+  if ((st = check_k(K, SVDQ_INT4))) return st;
+  if ((st = current_device_ok())) return st;
+  return hip_status(svdq_launch_gemm_w4a16(x, wq, ws, bias, y, M, N, K, stream));
+}
+
 int svdq_unfused_linear(const void* x, int M, int K, const float* smooth_inv, const void* lora_down, int rank,
                         const uint8_t* wq, const void* ws, const void* lora_up, const void* bias, int N,
                         int precision, uint8_t* xq, void* xs, float* lora_act, void* y, void* stream) {

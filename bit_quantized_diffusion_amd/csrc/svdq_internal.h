@@ -50,6 +50,8 @@ int svdq_launch_mlp_gemm_gelu_quant(const uint8_t* xq, const void* xs, const uin
                                     const float* lora_act, const void* lora_up, const void* bias, int M, int N, int K,
                                     int rank, const float* smooth_inv2, const void* lora_down2, int rank2,
                                     uint8_t* xq2, void* xs2, float* lora_act2, void* stream);
+int svdq_launch_gemm_w4a16(const void* x, const uint8_t* wq, const void* ws, const void* bias, void* y, int M,
+                           int N, int K, void* stream);
 int svdq_launch_unfused_linear(const void* x, int M, int K,
                                const float* smooth_inv, const void* lora_down,
                                int rank, const uint8_t* wq, const void* ws,

@@ -1113,6 +1113,149 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
                           wm, l32, h, tid, mo);
 }
 
+// ---------------------------------------------------------------------------
+// W4A16 comparison GEMM: 4-bit weights (the layer's INT4 codes and fp16
+// group scales), bf16 activations, bf16 matrix-core products.
+//
+// Same tiling, XCD map, two-slot ring and epilogue as the 4-bit kernels; a
+// stage is one K-group of 64.  The loader turns each 16 packed bytes of W
+// into 32 bf16 weights on their way into LDS: the code words give the FP8
+// images of q * 2^-9 (E = w & 0x87878787, O = rotr32(w, 4) & 0x87878787),
+// v_cvt_pk_f32_fp8 decodes them exactly, the product with s * 2^9 is q * s
+// exactly in fp32 and one rounding makes it bf16.  X tiles go to LDS as
+// they are.  v_mfma_f32_32x32x16_bf16 accumulates in fp32.
+// ---------------------------------------------------------------------------
+constexpr int kW16Row = 64 * 2 + 16;            // LDS row: 64 bf16 + 16 bytes padding
+constexpr int kW16Slot = 2 * kTile * kW16Row;   // W rows, then X rows
+static_assert(2 * kW16Slot >= kTile * kMxYRow * 2, "output staging fits in the ring");
+
+__global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_w4a16(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N, int K) {
+  __shared__ __attribute__((aligned(16))) int8_t lds_c[2][kW16Slot];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+  const int wn = wave >> 1, wm = wave & 1;
+  const int G = K / 64;
+  const size_t kb = static_cast<size_t>(K / 2);
+
+  const TileCoord tc = tile_coord(blockIdx.x, (N + kTile - 1) / kTile, (M + kTile - 1) / kTile);
+  const int n0 = tc.n0, m0 = tc.m0;
+
+  // W: thread t dequantizes half (t%2) of the group's 64 codes of row t/2;
+  // rows past the matrix edge are clamped to its last row (never stored)
+  const int wr = tid >> 1, wc = tid & 1;
+  const int wrow = min(n0 + wr, N - 1);
+  const uint8_t* wsrc = wq + static_cast<size_t>(wrow) * kb + wc * 16;
+  const uint16_t* wsc = ws + wrow;
+  const int wdst = wr * kW16Row + wc * 64;
+  // X: rows wave*32 + 8i + lane/8 (i = 0..3), 16-byte chunk lane%8 of the
+  // group's 128 bytes (eight lanes per row)
+  const int xr = wave * 32 + (lane >> 3), xc = lane & 7;
+  const uint16_t* xsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xsrc[i] = x + static_cast<size_t>(min(m0 + xr + 8 * i, M - 1)) * K + xc * 8;
+  const int xdst = kTile * kW16Row + xr * kW16Row + xc * 16;
+
+  struct LoadRegs {
+    uint4 w, x0, x1, x2, x3;
+    uint32_t s;
+  };
+  auto gload = [&](int g) {
+    LoadRegs L;
+    L.w = *reinterpret_cast<const uint4*>(wsrc + g * 32);
+    L.s = wsc[static_cast<size_t>(g) * N];
+    L.x0 = *reinterpret_cast<const uint4*>(xsrc[0] + g * 64);
+    L.x1 = *reinterpret_cast<const uint4*>(xsrc[1] + g * 64);
+    L.x2 = *reinterpret_cast<const uint4*>(xsrc[2] + g * 64);
+    L.x3 = *reinterpret_cast<const uint4*>(xsrc[3] + g * 64);
+    return L;
+  };
+  auto lstore = [&](auto buf_c, LoadRegs L) {
+    constexpr int buf = decltype(buf_c)::value;
+    const float sc = f16_bits_to_f32(L.s) * 512.0f;        // s * 2^9
+    const uint32_t w4[4] = {L.w.x, L.w.y, L.w.z, L.w.w};
+    uint32_t o[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t E = w4[i] & 0x87878787u;
+      const uint32_t O = __builtin_amdgcn_alignbit(w4[i], w4[i], 4) & 0x87878787u;
+      const v2f e01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(E), false);   // k 8i+0, 8i+2
+      const v2f e23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(E), true);    // k 8i+4, 8i+6
+      const v2f o01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(O), false);   // k 8i+1, 8i+3
+      const v2f o23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(O), true);    // k 8i+5, 8i+7
+      o[4 * i + 0] = cvt_pk_bf16(e01[0] * sc, o01[0] * sc);
+      o[4 * i + 1] = cvt_pk_bf16(e01[1] * sc, o01[1] * sc);
+      o[4 * i + 2] = cvt_pk_bf16(e23[0] * sc, o23[0] * sc);
+      o[4 * i + 3] = cvt_pk_bf16(e23[1] * sc, o23[1] * sc);
+    }
+    uint4* wd = reinterpret_cast<uint4*>(&lds_c[buf][0] + wdst);
+    wd[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    wd[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    wd[2] = make_uint4(o[8], o[9], o[10], o[11]);
+    wd[3] = make_uint4(o[12], o[13], o[14], o[15]);
+    int8_t* xd = &lds_c[buf][0] + xdst;
+    *reinterpret_cast<uint4*>(xd) = L.x0;
+    *reinterpret_cast<uint4*>(xd + 8 * kW16Row) = L.x1;
+    *reinterpret_cast<uint4*>(xd + 16 * kW16Row) = L.x2;
+    *reinterpret_cast<uint4*>(xd + 24 * kW16Row) = L.x3;
+  };
+
+  v16f acc[2][2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it)
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[it][jt][r] = 0.f;
+
+  // 16-k step s of the group: lane half h holds k 16s + 8h .. +8 of its row
+  auto compute = [&](auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    const int8_t* wb = &lds_c[buf][0] + (wn * 64 + l32) * kW16Row + 16 * h;
+    const int8_t* xb = &lds_c[buf][kTile * kW16Row] + (wm * 64 + l32) * kW16Row + 16 * h;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      v4i a[2], b[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        a[t] = *reinterpret_cast<const v4i*>(wb + t * 32 * kW16Row + 32 * s);
+        b[t] = *reinterpret_cast<const v4i*>(xb + t * 32 * kW16Row + 32 * s);
+      }
+#pragma unroll
+      for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+          acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a[it]),
+                                                                __builtin_bit_cast(v8bf, b[jt]), acc[it][jt], 0, 0, 0);
+    }
+  };
+
+  LoadRegs ld = gload(0);
+  lstore(Slot<0>{}, ld);
+  if (G > 1) ld = gload(1);
+  __syncthreads();
+
+  auto iteration = [&](int g, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    if (g + 1 < G) lstore(Slot<1 - buf>{}, ld);
+    if (g + 2 < G) ld = gload(g + 2);
+    compute(buf_c);
+    __syncthreads();
+  };
+  for (int g = 0; g < G; g += 2) {
+    iteration(g, Slot<0>{});
+    if (g + 1 < G) iteration(g + 1, Slot<1>{});
+  }
+
+  epilogue_tile128<0>(acc, reinterpret_cast<uint16_t*>(&lds_c[0][0]), nullptr, nullptr, bias, y, M, N, 0, n0, m0, wn,
+                      wm, l32, h, tid, MlpOut{});
+}
+
 // K1 grid: 64-row blocks x K slices.  The slice count is chosen so that
 // the grid holds about four workgroups per CU (256 CUs), with slices of
 // whole 128-k steps.
@@ -1308,6 +1451,15 @@ extern "C" int svdq_launch_mlp_gemm_gelu_quant(const uint8_t* xq, const void* xs
                      static_cast<const uint16_t*>(xs), wq, static_cast<const uint16_t*>(ws), lora_act,
                      static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias), nullptr, M, N, K, rank,
                      0, 0, 0, 0, nullptr, mo);
+  return static_cast<int>(hipGetLastError());
+}
+
+extern "C" int svdq_launch_gemm_w4a16(const void* x, const uint8_t* wq, const void* ws, const void* bias, void* y,
+                                      int M, int N, int K, void* stream) {
+  const int tiles = ((N + kTile - 1) / kTile) * ((M + kTile - 1) / kTile);
+  hipLaunchKernelGGL(k2_gemm_w4a16, dim3(tiles), dim3(kMxThreads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint16_t*>(x), wq, static_cast<const uint16_t*>(ws),
+                     static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), M, N, K);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -584,3 +584,21 @@ extern "C" int svdq_merge_lora(const uint16_t* lora_down, const uint16_t* lora_u
   }
   return SVDQ_OK;
 }
+
+// W4A16 comparison layer: the weights quantized with the layer's INT4 rule
+// per output channel in groups of 64 along K, with no smoothing and no
+// low-rank branch (the 4-bit weight-only baseline the SVDQuant abstract
+// measures W4A4 against).
+extern "C" int svdq_pack_w4a16(const uint16_t* w_bf16, int K, int N, uint8_t* wq, void* ws) {
+  if (!w_bf16 || !wq || !ws) return SVDQ_ERR_INVALID_ARG;
+  if (N < 1) return SVDQ_ERR_SHAPE;
+  int st;
+  if ((st = check_k(K, SVDQ_INT4))) return st;
+  uint16_t* wsb = static_cast<uint16_t*>(ws);
+  parallel_for(N, [&](int64_t n) {
+    std::vector<float> row(K);
+    for (int k = 0; k < K; ++k) row[k] = bf16_bits_to_f32(w_bf16[n * K + k]);
+    quant_int4_row(row.data(), K, wq + n * (K / 2), wsb + n, N);
+  }, 16);
+  return SVDQ_OK;
+}

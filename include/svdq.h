@@ -234,6 +234,21 @@ SVDQ_API int svdq_mlp_gemm_gelu_quant(const uint8_t* xq, const void* xs,
                            int precision, uint8_t* xq2, void* xs2, float* lora_act2,
                            void* stream);
 
+/* W4A16 comparison layer: 4-bit weights, bf16 activations (the 4-bit
+ * weight-only baseline that the SVDQuant abstract measures W4A4 against:
+ * 3.0x with INT4, 3.1x with NVFP4, whole model).  The weights carry the
+ * layer's INT4 rule per output channel in groups of 64 along K, with no
+ * smoothing and no low-rank branch.
+ *
+ * svdq_pack_w4a16 (host): w_bf16 [N][K] -> wq [N][K/2] (same code layout as
+ *   the W4A4 codes), ws [K/64][N] fp16.  K % 64 == 0.
+ * svdq_gemm_w4a16 (device): y [M][N] bf16 = bf16(x . (q s)^T + bias); x
+ *   bf16 [M][K], bias bf16 [N] or NULL.  Each weight q*s is rounded to bf16
+ *   once, the products accumulate in fp32. */
+SVDQ_API int svdq_pack_w4a16(const uint16_t* w_bf16, int K, int N, uint8_t* wq, void* ws);
+SVDQ_API int svdq_gemm_w4a16(const void* x, const uint8_t* wq, const void* ws,
+                             const void* bias, void* y, int M, int N, int K, void* stream);
+
 /* Unfused baseline of the same layer, for measuring what the two fusions
  * save (model card "svdq-int4-flux.1-dev", Nunchaku engine caption (a): a
  * naive low-rank branch as separate kernels costs an extra 16-bit read of

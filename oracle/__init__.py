@@ -7,3 +7,4 @@ Python binding) never calls it and shares no code with it.
 
 from .svdq_oracle import *  # noqa: F401,F403
 from .mxfp4_oracle import *  # noqa: F401,F403
+from .w4a16_oracle import *  # noqa: F401,F403

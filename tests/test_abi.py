@@ -129,6 +129,21 @@ def test_mlp_calls_validate():
     assert call(a12=None, a13=0, a17=None) != bq.SVDQ_ERR_INVALID_ARG   # rank2 == 0 needs no L1 / lora_act2
 
 
+def test_w4a16_calls_validate():
+    """The W4A16 comparison GEMM and its pack: NULL / misaligned pointers,
+    K not a multiple of 64, empty shapes."""
+    g = bq.lib.svdq_gemm_w4a16
+    assert g(None, FAKE, FAKE, None, FAKE, 16, 16, 64, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert g(FAKE, FAKE, None, None, FAKE, 16, 16, 64, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert g(FAKE, FAKE, FAKE, MIS, FAKE, 16, 16, 64, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert g(FAKE, FAKE, FAKE, None, FAKE, 16, 16, 96, None) == bq.SVDQ_ERR_SHAPE
+    assert g(FAKE, FAKE, FAKE, None, FAKE, 0, 16, 64, None) == bq.SVDQ_ERR_SHAPE
+    assert g(FAKE, FAKE, FAKE, None, FAKE, 16, 0, 64, None) == bq.SVDQ_ERR_SHAPE
+    p = bq.lib.svdq_pack_w4a16
+    assert p(None, 64, 4, FAKE, FAKE) == bq.SVDQ_ERR_INVALID_ARG
+    assert p(FAKE, 100, 4, FAKE, FAKE) == bq.SVDQ_ERR_SHAPE
+
+
 @pytest.mark.skipif(_gpu_present(), reason="checks the no-device path")
 def test_no_device_gives_unsupported_device_not_a_crash():
     L = bq.lib
