@@ -58,10 +58,8 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
 }
 
-// fp32 -> packed bf16 pair with round to nearest even (bit arithmetic)
-__device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
-  return bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
-}
+// fp32 -> packed bf16 pair with round to nearest even
+__device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) { return cvt_pk_bf16(lo, hi); }
 
 // ---------------------------------------------------------------------------
 // Kernel 1: smoothing + INT4 activation quantization + down projection.
@@ -401,6 +399,19 @@ __global__ void fill_zero_f32(float* __restrict__ p, size_t n) {
 constexpr int kTile = 128;      // output tile edge (both n and m)
 constexpr unsigned kUnitScales = 0x7F7F7F7Fu;   // E8M0 127 = 1.0 in every byte
 
+// Raw buffer resource over [base, base + bytes) (bytes clamped to 32 bits;
+// callers keep every access inside the range).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
+  const int n = static_cast<int>(bytes > 0xFFFFFFFFull ? 0xFFFFFFFFull : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n, 0x00020000);
+}
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 buffer_load_u4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -680,13 +691,13 @@ __device__ __forceinline__ void epilogue_tile128(v16f (&acc)[2][2], uint16_t* __
       for (int j = 0; j < 4; ++j) {
         const int ml = wm * 64 + jt * 32 + l32;
         const int nl = wn * 64 + it * 32 + 8 * j + 4 * h;
-        uint32_t hv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          hv[i] = bf16_rne_bits(acc[it][jt][4 * j + i] + bv[it][j][i]);
-          if constexpr (EPI >= 1) hv[i] = bf16_rne_bits(gelu_tanh_f32(__uint_as_float(hv[i] << 16)));
+        uint32_t p01 = cvt_pk_bf16(acc[it][jt][4 * j + 0] + bv[it][j][0], acc[it][jt][4 * j + 1] + bv[it][j][1]);
+        uint32_t p23 = cvt_pk_bf16(acc[it][jt][4 * j + 2] + bv[it][j][2], acc[it][jt][4 * j + 3] + bv[it][j][3]);
+        if constexpr (EPI >= 1) {
+          p01 = cvt_pk_bf16(gelu_tanh_f32(__uint_as_float(p01 << 16)), gelu_tanh_f32(__uint_as_float(p01 & 0xFFFF0000u)));
+          p23 = cvt_pk_bf16(gelu_tanh_f32(__uint_as_float(p23 << 16)), gelu_tanh_f32(__uint_as_float(p23 & 0xFFFF0000u)));
         }
-        *reinterpret_cast<uint2*>(stg + ml * kMxYRow + nl) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+        *reinterpret_cast<uint2*>(stg + ml * kMxYRow + nl) = make_uint2(p01, p23);
       }
   __syncthreads();
 
@@ -883,7 +894,7 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_mxfp4(
 // so that v_mfma_scale_f32_32x32x64_f8f6f4 returns the group's exact integer
 // partial P scaled by 2^(e_w + e_x) (exponents of the two scales applied as
 // E8M0 block scales, with 2^18 on the W side to cancel the code encoding).
-// The scale significands in [1, 2) multiply in packed fp16 and
+// The scale significands in [0.5, 1) multiply in packed fp16 and
 // v_fma_mix_f32 adds P' * (m_w m_x) into the fp32 accumulators.
 //
 // DEBUG = true is a test hook on the same loader, LDS layout and MFMA path:
@@ -929,23 +940,34 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
     m0 = tc.m0;
   }
 
+  // Loads go through buffer resources based at the tile's first row (and at
+  // the scale array), so that a stage needs no address arithmetic: a fixed
+  // per-lane offset plus the stage's offset in a scalar register.  Every
+  // access stays inside the resource's range by construction.
   // code loads: rows wave*32 + 16i + lane/4 (i = 0, 1) of W and X, 16-byte
   // chunk lane%4 of the stage's 64 bytes; rows clamped into the matrix
   const int lr = wave * 32 + (lane >> 2), lc = lane & 3;
-  const uint8_t* wsrc0 = wq + static_cast<size_t>(min(n0 + lr, N - 1)) * kb + lc * 16;
-  const uint8_t* wsrc1 = wq + static_cast<size_t>(min(n0 + lr + 16, N - 1)) * kb + lc * 16;
-  const uint8_t* xsrc0 = xq + static_cast<size_t>(min(m0 + lr, M - 1)) * kb + lc * 16;
-  const uint8_t* xsrc1 = xq + static_cast<size_t>(min(m0 + lr + 16, M - 1)) * kb + lc * 16;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wq + static_cast<size_t>(n0) * kb, static_cast<size_t>(N - n0) * kb);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(xq + static_cast<size_t>(m0) * kb, static_cast<size_t>(M - m0) * kb);
+  const int vw0 = min(lr, N - 1 - n0) * static_cast<int>(kb) + lc * 16;
+  const int vw1 = min(lr + 16, N - 1 - n0) * static_cast<int>(kb) + lc * 16;
+  const int vx0 = min(lr, M - 1 - m0) * static_cast<int>(kb) + lc * 16;
+  const int vx1 = min(lr + 16, M - 1 - m0) * static_cast<int>(kb) + lc * 16;
   const int ldst = lr * kI4Row + lc * 32;
-  // scale loads: threads 0..127 W, 128..255 X; group (t/64)%2 of the stage,
-  // rows 2(t%64), 2(t%64)+1 (one dword where both rows are in the matrix
-  // and aligned, else two halves from rows clamped into the matrix)
-  const bool s_is_w = tid < kTile;
-  const int sg = (tid >> 6) & 1, sr = (tid & 63) * 2;
+  // scale loads: threads 0..127 (waves 0, 1) W, 128..255 (waves 2, 3) X;
+  // group (t/64)%2 of the stage, rows 2(t%64), 2(t%64)+1: one dword when
+  // the row count is even (pair clamped to the last two rows), else two
+  // halves from rows clamped into the matrix
+  const bool s_is_w = wave < 2;                // wave-uniform
+  const int sg = wave & 1, sr = (tid & 63) * 2;
   const int s_rows = s_is_w ? N : M;
   const int s_r0 = (s_is_w ? n0 : m0) + sr;
-  const uint16_t* s_base = s_is_w ? ws : xs;
-  const bool s_dw = (s_rows % 2) == 0 && s_r0 + 1 < s_rows;
+  const bool s_even = (s_rows % 2) == 0;
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(s_is_w ? ws : xs, static_cast<size_t>(G) * static_cast<size_t>(s_rows) * 2);
+  const int vs0 = 2 * (s_even ? min(s_r0, s_rows - 2) : min(s_r0, s_rows - 1));
+  const int vs1 = 2 * min(s_r0 + 1, s_rows - 1);
+  const int vsg = 2 * sg * s_rows;
 
   struct LoadRegs {
     uint4 w0, w1, x0, x1;
@@ -955,30 +977,33 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   // lanes of that group re-read the first one (never used)
   auto gload = [&](int st) {
     LoadRegs L;
-    const bool two = 2 * st + 1 < G;
-    const int off = st * (kI4Stage / 2) - (two || lc < 2 ? 0 : 32);
-    L.w0 = *reinterpret_cast<const uint4*>(wsrc0 + off);
-    L.w1 = *reinterpret_cast<const uint4*>(wsrc1 + off);
-    L.x0 = *reinterpret_cast<const uint4*>(xsrc0 + off);
-    L.x1 = *reinterpret_cast<const uint4*>(xsrc1 + off);
+    const int so = st * (kI4Stage / 2);
+    const int sso = 4 * st * s_rows;
+    int a = 0, g1 = vsg;
+    if (2 * st + 1 >= G) {
+      a = lc < 2 ? 0 : 32;
+      g1 = 0;
+    }
+    L.w0 = buffer_load_u4(rw, vw0 - a, so);
+    L.w1 = buffer_load_u4(rw, vw1 - a, so);
+    L.x0 = buffer_load_u4(rx, vx0 - a, so);
+    L.x1 = buffer_load_u4(rx, vx1 - a, so);
     L.s = 0;
     if constexpr (!DEBUG) {
-      const uint16_t* col = s_base + static_cast<size_t>(2 * st + (two ? sg : 0)) * s_rows;
-      if (s_dw) {
-        L.s = *reinterpret_cast<const uint32_t*>(col + s_r0);
+      if (s_even) {
+        L.s = __builtin_amdgcn_raw_buffer_load_b32(rs, g1 + vs0, sso, 0);
       } else {
-        L.s = static_cast<uint32_t>(col[min(s_r0, s_rows - 1)]) |
-              (static_cast<uint32_t>(col[min(s_r0 + 1, s_rows - 1)]) << 16);
+        L.s = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rs, g1 + vs0, sso, 0)) |
+              (static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rs, g1 + vs1, sso, 0)) << 16);
       }
     }
     return L;
   };
-  // A scale s (fp16 >= 0) splits into its binary exponent, which the matrix
-  // core applies exactly as an E8M0 block scale, and its significand in
-  // [1, 2), an exact fp16; both from the fp32 image of s (normal for every
-  // fp16 value).  W rows carry an extra 2^18 that cancels the 2^-18 of the
-  // FP8 code encoding.  s == 0 gives byte 0 (2^-127) with significand 1;
-  // its codes are zero, so are its products.
+  // A scale s (fp16 >= 0) splits as s = m * 2^e with m in [0.5, 1)
+  // (v_frexp_mant_f16, v_frexp_exp_i16_f16, subnormals included): 2^e is
+  // applied exactly by the matrix core as an E8M0 block scale, m is an
+  // exact fp16.  W rows carry an extra 2^18 that cancels the 2^-18 of the
+  // FP8 code encoding.  s == 0 gives m = 0; its codes are zero too.
   auto lstore = [&](auto buf_c, LoadRegs L) {
     constexpr int buf = decltype(buf_c)::value;
     int8_t* wd = &lds_c[buf][0] + ldst;
@@ -992,9 +1017,9 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
     _Float16 sm[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const uint32_t u = __float_as_uint(f16_bits_to_f32((L.s >> (16 * i)) & 0xFFFFu));
-      eb[i] = ((u >> 23) & 0xFFu) + (s_is_w && u != 0 ? 18u : 0u);
-      sm[i] = static_cast<_Float16>(__uint_as_float((u & 0x007FFFFFu) | 0x3F800000u));
+      const _Float16 sv = __builtin_bit_cast(_Float16, static_cast<uint16_t>(L.s >> (16 * i)));
+      eb[i] = static_cast<uint32_t>(__builtin_amdgcn_frexp_exph(sv) + (s_is_w ? 127 + 18 : 127)) & 0xFFu;
+      sm[i] = __builtin_amdgcn_frexp_manth(sv);
     }
     *reinterpret_cast<uint16_t*>(&lds_e[buf][s_is_w ? 0 : 1][sg][sr]) = static_cast<uint16_t>(eb[0] | (eb[1] << 8));
     *reinterpret_cast<h2*>(&lds_m[buf][s_is_w ? 0 : 1][sg][sr]) = h2{sm[0], sm[1]};
@@ -1007,6 +1032,107 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[it][jt][r] = 0.f;
+
+  // Both groups of a stage as one software pipeline over its 8 tile-groups
+  // (2 groups x 2 x 2 tiles): the MFMA of tile-group t+1 is issued before
+  // the dequant of tile-group t, and the second group's LDS operands are
+  // read while the first group computes.  sched_group_barrier states that
+  // order: left alone, the scheduler puts each dequant right behind the
+  // MFMA that feeds it and the VALU waits for the matrix core at every tile.
+  struct Ops {
+    v8i a0, a1, b0, b1;
+    uint32_t ea0, ea1, eb0, eb1;
+    h2 mx0, mx1;
+    uint2 w00, w01, w02, w03, w10, w11, w12, w13;
+  };
+  auto load_ops = [&](auto buf_c, auto g_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    constexpr int g = decltype(g_c)::value;
+    Ops o;
+    const int8_t* wr = &lds_c[buf][0] + (wn * 64 + l32) * kI4Row + 64 * g + 32 * h;
+    const int8_t* xr = &lds_c[buf][kTile * kI4Row] + (wm * 64 + l32) * kI4Row + 64 * g + 32 * h;
+    auto rd = [](const int8_t* q) {
+      return __builtin_shufflevector(*reinterpret_cast<const v4i*>(q), *reinterpret_cast<const v4i*>(q + 16), 0, 1, 2,
+                                     3, 4, 5, 6, 7);
+    };
+    o.a0 = rd(wr);
+    o.a1 = rd(wr + 32 * kI4Row);
+    o.b0 = rd(xr);
+    o.b1 = rd(xr + 32 * kI4Row);
+    o.ea0 = lds_e[buf][0][g][wn * 64 + l32];
+    o.ea1 = lds_e[buf][0][g][wn * 64 + 32 + l32];
+    o.eb0 = lds_e[buf][1][g][wm * 64 + l32];
+    o.eb1 = lds_e[buf][1][g][wm * 64 + 32 + l32];
+    const _Float16 m0x = lds_m[buf][1][g][wm * 64 + l32];
+    const _Float16 m1x = lds_m[buf][1][g][wm * 64 + 32 + l32];
+    o.mx0 = h2{m0x, m0x};
+    o.mx1 = h2{m1x, m1x};
+    const _Float16* mwp = &lds_m[buf][0][g][wn * 64 + 4 * h];
+    o.w00 = *reinterpret_cast<const uint2*>(mwp + 0);
+    o.w01 = *reinterpret_cast<const uint2*>(mwp + 8);
+    o.w02 = *reinterpret_cast<const uint2*>(mwp + 16);
+    o.w03 = *reinterpret_cast<const uint2*>(mwp + 24);
+    o.w10 = *reinterpret_cast<const uint2*>(mwp + 32);
+    o.w11 = *reinterpret_cast<const uint2*>(mwp + 40);
+    o.w12 = *reinterpret_cast<const uint2*>(mwp + 48);
+    o.w13 = *reinterpret_cast<const uint2*>(mwp + 56);
+    return o;
+  };
+  auto mf2 = [&](const Ops& o, auto t_c) {
+    constexpr int t = decltype(t_c)::value;
+    constexpr int it = t >> 1, jt = t & 1;
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(it ? o.a1 : o.a0, jt ? o.b1 : o.b0, v16f{}, 0, 0, 0,
+                                                           it ? o.ea1 : o.ea0, 0, jt ? o.eb1 : o.eb0);
+  };
+  auto dq2 = [&](const Ops& o, auto t_c, const v16f& p) {
+    constexpr int t = decltype(t_c)::value;
+    constexpr int it = t >> 1, jt = t & 1;
+    const h2 mx = jt ? o.mx1 : o.mx0;
+    const uint2 mw[4] = {it ? o.w10 : o.w00, it ? o.w11 : o.w01, it ? o.w12 : o.w02, it ? o.w13 : o.w03};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const h2 s01 = __builtin_bit_cast(h2, mw[j].x) * mx;
+      const h2 s23 = __builtin_bit_cast(h2, mw[j].y) * mx;
+      acc[it][jt][4 * j + 0] = __builtin_fmaf(p[4 * j + 0], static_cast<float>(s01[0]), acc[it][jt][4 * j + 0]);
+      acc[it][jt][4 * j + 1] = __builtin_fmaf(p[4 * j + 1], static_cast<float>(s01[1]), acc[it][jt][4 * j + 1]);
+      acc[it][jt][4 * j + 2] = __builtin_fmaf(p[4 * j + 2], static_cast<float>(s23[0]), acc[it][jt][4 * j + 2]);
+      acc[it][jt][4 * j + 3] = __builtin_fmaf(p[4 * j + 3], static_cast<float>(s23[1]), acc[it][jt][4 * j + 3]);
+    }
+  };
+  using I0 = Slot<0>;
+  using I1 = Slot<1>;
+  using I2 = Slot<2>;
+  using I3 = Slot<3>;
+  // pin: the MFMA that produced pn is issued before the dequant that
+  // updates acc[it][jt] (the asm reads pn's registers only nominally)
+  auto pin = [](v16f& pn, v16f& a) { asm volatile("" : "+v"(pn), "+v"(a)); };
+  auto two_groups = [&](auto buf_c) {
+    const Ops o0 = load_ops(buf_c, I0{});
+    v16f pa = mf2(o0, I0{});
+    v16f pb = mf2(o0, I1{});
+    pin(pb, acc[0][0]);
+    dq2(o0, I0{}, pa);
+    pa = mf2(o0, I2{});
+    pin(pa, acc[0][1]);
+    dq2(o0, I1{}, pb);
+    pb = mf2(o0, I3{});
+    pin(pb, acc[1][0]);
+    const Ops o1 = load_ops(buf_c, I1{});
+    dq2(o0, I2{}, pa);
+    pa = mf2(o1, I0{});
+    pin(pa, acc[1][1]);
+    dq2(o0, I3{}, pb);
+    pb = mf2(o1, I1{});
+    pin(pb, acc[0][0]);
+    dq2(o1, I0{}, pa);
+    pa = mf2(o1, I2{});
+    pin(pa, acc[0][1]);
+    dq2(o1, I1{}, pb);
+    pb = mf2(o1, I3{});
+    pin(pb, acc[1][0]);
+    dq2(o1, I2{}, pa);
+    dq2(o1, I3{}, pb);
+  };
 
   // group g of the stage: FP8 bytes 64g + 32h of the row for lane half h
   auto compute = [&](auto buf_c, bool one, int g0) {
@@ -1087,6 +1213,12 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
       dq(2, p0);
       dq(3, p1);
     };
+    if constexpr (!DEBUG) {
+      if (!one) {
+        two_groups(buf_c);
+        return;
+      }
+    }
     group(Slot<0>{});
     if (!one) group(Slot<1>{});
   };
