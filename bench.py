@@ -24,6 +24,10 @@ matrix-core peak.  The `w4a16` object times the same weights as a 4-bit
 weight-only layer (bf16 activations, one kernel) against the dense bf16
 matrix-core peak, the comparison the pages quote W4A4 speedups against.
 
+Each roofline object also carries `measured_ceiling`: the dense rate the
+matrix core sustains here on independent MFMAs of the same instruction
+(FP8, or FP4 for MXFP4), and the fraction of it achieved.
+
 `--calibrate-copy` instead runs a plain elementwise copy of 1 GiB a few
 times; its FETCH_SIZE / WRITE_SIZE counters give the factor that turns the
 counters read on the GEMM into HBM bytes.
@@ -142,7 +146,8 @@ def main():
     ax1 = x1.float().abs().amax(dim=0).cpu().numpy().astype(np.float32)
     t0 = time.time()
     pk1 = bq.pack_weights(lay1["w"], ax1, s1.rank)
-    log(f"bench: packed fc1 ({s1.K}x{s1.N}, rank {s1.rank}) in {time.time() - t0:.1f} s")
+    pack_s = {"fc1": round(time.time() - t0, 2)}
+    log(f"bench: packed fc1 ({s1.K}x{s1.N}, rank {s1.rank}) in {pack_s['fc1']:.1f} s")
     L1 = bq.PackedLinear.from_host(pk1, lay1["bias"], s1.rank, device=dev)
     y1 = bq.linear(x1, L1)
     x2 = torch.nn.functional.gelu(y1.float(), approximate="tanh").to(torch.bfloat16)
@@ -151,7 +156,8 @@ def main():
     w2 = synth.gen_w(s2, idx2)
     t0 = time.time()
     pk2 = bq.pack_weights(w2, ax2, s2.rank)
-    log(f"bench: packed fc2 ({s2.K}x{s2.N}, rank {s2.rank}) in {time.time() - t0:.1f} s")
+    pack_s["fc2"] = round(time.time() - t0, 2)
+    log(f"bench: packed fc2 ({s2.K}x{s2.N}, rank {s2.rank}) in {pack_s['fc2']:.1f} s")
     L2 = bq.PackedLinear.from_host(pk2, synth.gen_bias(s2), s2.rank, device=dev)
     torch.cuda.synchronize()
 
@@ -242,6 +248,10 @@ def main():
                 "traffic_source": TRAFFIC_NOTE if traffic is not None else
                 ("counter summary taken on older kernel source" if traffic_state == "stale" else None)}
 
+    ceil8 = mfma_ceiling(bq, torch, stream, bq.INT4)
+    roofline["measured_ceiling"] = ceil8
+    roofline["frac_of_measured_ceiling"] = round(achieved / ceil8["tops"], 4)
+
     ablation = None
     if not args.no_ablation:
         ablation = fusion_ablation(bq, torch, np, sets, M, (s1, s2), per, stream, reps=10)
@@ -254,6 +264,9 @@ def main():
     if not args.no_mxfp4:
         mx = mxfp4_layers(bq, torch, np, dev, (s1, s2), (lay1["w"], w2), (ax1, ax2),
                           (lay1["bias"], synth.gen_bias(s2)), (x1, x2), args.sets, stream, reps=20)
+        ceil4 = mfma_ceiling(bq, torch, stream, bq.MXFP4)
+        mx["roofline"]["measured_ceiling"] = ceil4
+        mx["roofline"]["frac_of_measured_ceiling"] = round(mx["roofline"]["achieved"] / ceil4["tops"], 4)
 
     w16 = None
     if not args.no_w4a16:
@@ -279,6 +292,7 @@ def main():
         "mxfp4": mx,
         "mlp_fusion": mlp,
         "w4a16": w16,
+        "offline_pack_s": pack_s,
     }
     print(json.dumps(out), flush=True)
 
@@ -488,6 +502,28 @@ def w4a16_layers(bq, torch, np, dev, specs, ws, biases, xs, n_sets, stream, per,
                        "peak_basis": "dense bf16 matrix-core rate, 256 CU x 2.4 GHz x 4096 flops/clk"}
     log(f"bench: w4a16 {json.dumps(out)}")
     return out
+
+
+def mfma_ceiling(bq, torch, stream, precision, reps=3):
+    """Dense matrix-core rate this GPU sustains: svdq_bench_mfma_ceiling
+    (independent 32x32x64 scaled MFMAs, FP8 or FP4 operands, 2 waves per
+    SIMD), timed with HIP events on the library's stream."""
+    ops, out = bq.mfma_ceiling(precision)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        bq.mfma_ceiling(precision, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    tops = ops / min(ts) / 1e12
+    name = "FP8" if precision == bq.INT4 else "FP4"
+    res = {"tops": round(tops, 1), "kernel": f"k_mfma_ceiling ({name} 32x32x64 scaled MFMA, 8 independent "
+                                             "accumulators per wave, 2 waves per SIMD)"}
+    log(f"bench: measured {name} matrix-core ceiling {res['tops']} TOPS")
+    return res
 
 
 def cpu_baseline(lay1, pk1, spec, seconds, chunk):

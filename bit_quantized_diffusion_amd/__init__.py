@@ -29,7 +29,7 @@ __all__ = [
     "version", "device_check", "packed_sizes", "act_sizes", "pack_weights",
     "quantize_act_lora_down", "gemm_w4a4_lora_up", "debug_group_partials", "unfused_linear",
     "PackedLinear", "linear", "gemm_w4a4_lora_up_gelu", "mlp_gemm_gelu_quant", "mlp",
-    "pack_w4a16", "gemm_w4a16",
+    "pack_w4a16", "gemm_w4a16", "mfma_ceiling",
 ]
 
 
@@ -242,6 +242,17 @@ def mlp_gemm_gelu_quant(xq, xs, wq, ws, lora_act, lora_up, bias, M: int, N: int,
         _dptr(xq2, torch.uint8, (M, N // 2), "xq2"), _dptr(xs2, torch.float16, (N // 64, M), "xs2"),
         _dptr(lora_act2, torch.float32, (M, rank2), "lora_act2") if rank2 else None, _stream(dev)))
     return xq2, xs2, (lora_act2 if rank2 else None)
+
+
+def mfma_ceiling(precision: int = INT4, blocks: int = 512, iters: int = 4096, out=None):
+    """Launch the matrix-core ceiling kernel once (measurement only); returns
+    (ops per launch, the checksum tensor).  The caller times the launch."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((blocks,), dtype=torch.float32, device="cuda")
+    check(lib.svdq_bench_mfma_ceiling(precision, blocks, iters, _dptr(out, torch.float32, (blocks,), "out"),
+                                      _stream(out.device)))
+    return float(blocks) * 4 * 8 * iters * 131072, out
 
 
 def pack_w4a16(w_bf16: np.ndarray):

@@ -27,7 +27,7 @@ EXPORTED = (
     "svdq_quantize_act_lora_down", "svdq_gemm_w4a4_lora_up",
     "svdq_unfused_linear", "svdq_debug_group_partials", "svdq_merge_lora",
     "svdq_gemm_w4a4_lora_up_gelu", "svdq_mlp_gemm_gelu_quant",
-    "svdq_pack_w4a16", "svdq_gemm_w4a16",
+    "svdq_pack_w4a16", "svdq_gemm_w4a16", "svdq_bench_mfma_ceiling",
 )
 
 
@@ -66,6 +66,7 @@ def _load():
         "svdq_mlp_gemm_gelu_quant": ([vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, vp, i, i, vp, vp, vp, vp], i),
         "svdq_pack_w4a16": ([vp, i, i, vp, vp], i),
         "svdq_gemm_w4a16": ([vp, vp, vp, vp, vp, i, i, i, vp], i),
+        "svdq_bench_mfma_ceiling": ([i, i, i, vp, vp], i),
     }
     for name, (args, ret) in sig.items():
         fn = getattr(lib, name)

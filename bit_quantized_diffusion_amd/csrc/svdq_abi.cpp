@@ -219,6 +219,15 @@ int svdq_unfused_linear(const void* x, int M, int K, const float* smooth_inv, co
                                                precision, xq, xs, lora_act, y, stream));
 }
 
+int svdq_bench_mfma_ceiling(int precision, int blocks, int iters, float* out, void* stream) {
+  if (!out || !aligned16(out)) return SVDQ_ERR_INVALID_ARG;
+  if (precision != SVDQ_INT4 && precision != SVDQ_MXFP4) return SVDQ_ERR_INVALID_ARG;
+  if (blocks < 1 || iters < 1) return SVDQ_ERR_SHAPE;
+  int st;
+  if ((st = current_device_ok())) return st;
+  return hip_status(svdq_launch_mfma_ceiling(precision, blocks, iters, out, stream));
+}
+
 int svdq_debug_group_partials(const uint8_t* xq, const uint8_t* wq, int M, int N, int K, int m0, int n0, int mt,
                               int nt, int32_t* out, void* stream) {
   if (!xq || !wq || !out) return SVDQ_ERR_INVALID_ARG;

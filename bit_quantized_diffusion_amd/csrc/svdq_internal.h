@@ -58,6 +58,7 @@ int svdq_launch_unfused_linear(const void* x, int M, int K,
                                const void* lora_up, const void* bias, int N,
                                int precision, uint8_t* xq, void* xs,
                                float* lora_act, void* y, void* stream);
+int svdq_launch_mfma_ceiling(int precision, int blocks, int iters, float* out, void* stream);
 int svdq_launch_debug_group_partials(const uint8_t* xq, const uint8_t* wq,
                                      int M, int N, int K, int m0, int n0,
                                      int mt, int nt, int32_t* out,

@@ -266,6 +266,15 @@ SVDQ_API int svdq_unfused_linear(const void* x, int M, int K,
                         uint8_t* xq, void* xs, float* lora_act, void* y,
                         void* stream);
 
+/* Measurement hook: the dense matrix-core rate this GPU sustains.  Each of
+ * `blocks` workgroups (4 waves; launch two per CU) issues 8 * iters
+ * independent v_mfma_scale_f32_32x32x64_f8f6f4 per wave, with FP8 operands
+ * (precision SVDQ_INT4: the 8-bit rate the INT4 GEMM runs at) or FP4
+ * operands (SVDQ_MXFP4).  Ops per launch = blocks * 4 * 8 * iters * 131072;
+ * the caller times it.  out (dev) [blocks] fp32 receives one checksum per
+ * workgroup.  blocks, iters >= 1. */
+SVDQ_API int svdq_bench_mfma_ceiling(int precision, int blocks, int iters, float* out, void* stream);
+
 /* Test hook: the exact per-group integer partials of the INT4 GEMM for the
  * output window rows [m0, m0+mt) x columns [n0, n0+nt), computed by the
  * same device code as svdq_gemm_w4a4_lora_up.

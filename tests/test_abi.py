@@ -166,3 +166,14 @@ def test_pack_validates_on_host():
         bq.pack_weights(w, np.ones(100, np.float32), 16)
     with pytest.raises(ValueError):
         bq.pack_weights(np.zeros((64, 128), np.uint16), np.ones(64, np.float32), 16)
+
+
+def test_mfma_ceiling_validates():
+    """The measurement hook: NULL / misaligned output, unknown precision,
+    empty launch."""
+    f = bq.lib.svdq_bench_mfma_ceiling
+    assert f(bq.INT4, 4, 4, None, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert f(bq.INT4, 4, 4, MIS, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert f(7, 4, 4, FAKE, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert f(bq.INT4, 0, 4, FAKE, None) == bq.SVDQ_ERR_SHAPE
+    assert f(bq.MXFP4, 4, 0, FAKE, None) == bq.SVDQ_ERR_SHAPE
