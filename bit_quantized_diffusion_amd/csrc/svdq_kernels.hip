@@ -736,89 +736,86 @@ __device__ __forceinline__ v16f mfma_fp4(const v4i& a, const v4i& b, const v16f&
                                                          static_cast<int>(sb));
 }
 
+constexpr int kMxdRowB = 128;                      // LDS bytes per row and stage (no padding)
+constexpr int kMxdOp = kTile * kMxdRowB;           // one operand's rows
+constexpr int kMxdSlot = 2 * kMxdOp + 2 * 8 * kTile;   // W rows, X rows, then scales [W|X][block][row]
+static_assert(2 * kMxdSlot >= kTile * kMxYRow * 2, "output staging fits in the ring");
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_mxfp4(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws,
     const float* __restrict__ lact, const uint16_t* __restrict__ lup,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N, int K, int rank) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_c[2][kMxSlot];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_s[2][2][8][kTile];   // [slot][W|X][block][row]
+  __shared__ __attribute__((aligned(16))) uint8_t lds_c[2][kMxdSlot];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int h = lane >> 5;
-  const int wn = wave >> 1, wm = wave & 1;     // 2 x 2 waves: 64 n x 64 m each
+  const int wn = wave >> 1, wm = wave & 1;
   const int S = (K + kMxStage - 1) / kMxStage;
-  const bool half_last = (K % kMxStage) != 0;  // then K % 256 == 128
-  const size_t kb = static_cast<size_t>(K / 2);
+  const int kb = K / 2;
 
   const TileCoord tc = tile_coord(blockIdx.x, (N + kTile - 1) / kTile, (M + kTile - 1) / kTile);
   const int n0 = tc.n0, m0 = tc.m0;
 
-  // code loads: rows wave*32 + 8i + lane/8 of W and X, chunk lane%8; rows
-  // past the matrix edge are clamped to its last row (never stored)
-  const int lr = wave * 32 + (lane >> 3), lc = lane & 7;
-  const uint8_t* wsrc[4];
-  const uint8_t* xsrc[4];
+  // Direct-to-LDS loads.  Waves 0, 1 load W rows, waves 2, 3 X rows: load j
+  // of a wave fills rows 64 (wave % 2) + 8 j .. + 7 of its operand, lane i
+  // row + i/8, 16-byte LDS chunk i%8, which holds the row's chunk
+  // (i%8) ^ (row%8) (the XOR spreads a column of rows over the banks).
+  // Rows past the matrix edge are clamped to its last row; the resources
+  // bound every access.
+  const bool is_w = wave < 2;
+  const int rows = is_w ? N : M;
+  const int r0 = is_w ? n0 : m0;
+  const __amdgpu_buffer_rsrc_t rc =
+      make_rsrc(is_w ? wq : xq, static_cast<size_t>(rows) * static_cast<size_t>(kb));
+  const int lrow = 64 * (wave & 1) + (lane >> 3);          // + 8 j
+  int vcode[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    wsrc[i] = wq + static_cast<size_t>(min(n0 + lr + 8 * i, N - 1)) * kb + lc * 16;
-    xsrc[i] = xq + static_cast<size_t>(min(m0 + lr + 8 * i, M - 1)) * kb + lc * 16;
+  for (int j = 0; j < 8; ++j) {
+    const int r = lrow + 8 * j;
+    vcode[j] = min(r0 + r, rows - 1) * kb + (((lane & 7) ^ (r & 7)) << 4);
   }
-  const int ldst = lr * kMxRow + lc * 16;
-  // scale loads: thread t moves rows 4(t%32) .. +3 of block t/32 of the
-  // stage for W and for X; one dword where the 4 rows are inside the
-  // matrix and aligned, else 4 bytes from rows clamped into the matrix
-  const int sblk = tid >> 5, sr = (tid & 31) * 4;
-  const bool w_dw = (N % 4) == 0 && n0 + sr + 3 < N;
-  const bool x_dw = (M % 4) == 0 && m0 + sr + 3 < M;
-  auto scale4 = [&](const uint8_t* col, int r0, int rows, bool dw) -> uint32_t {
-    if (dw) return *reinterpret_cast<const uint32_t*>(col + r0);
-    uint32_t v = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v |= static_cast<uint32_t>(col[min(r0 + i, rows - 1)]) << (8 * i);
-    return v;
-  };
+  const int lds_op = is_w ? 0 : kMxdOp;
+  // scales of a stage: 8 blocks x 128 rows = 256 dwords per operand; the
+  // operand's two waves load dwords d = 128 i + 64 (wave % 2) + lane
+  // (i = 0, 1): block d / 32, rows 4 (d % 32) .. + 3, as one dword where
+  // the 4 rows are inside the matrix (row count a multiple of 4), else as
+  // bytes from rows clamped into the matrix
+  const __amdgpu_buffer_rsrc_t rsc =
+      make_rsrc(is_w ? ws : xs, static_cast<size_t>(K / 32) * static_cast<size_t>(rows));
+  const int srow = r0 + 4 * (lane & 31);
+  const bool s_dw = (rows % 4) == 0 && srow + 3 < rows;
+  const int lds_sc = 2 * kMxdOp + (is_w ? 0 : 8 * kTile);
 
-  struct LoadRegs {
-    uint4 w0, w1, w2, w3, x0, x1, x2, x3;
-    uint32_t s0, s1;
-  };
-  // stage st.  In a half stage the second 64 bytes of a row and the second
-  // scale dword are never read: those lanes re-read bytes inside the row.
-  auto gload = [&](int st) {
-    LoadRegs L;
-    const bool full = (st + 1) * kMxStageB <= static_cast<int>(kb);
-    const int off = st * kMxStageB - (full || lc < 4 ? 0 : kMxStageB / 2);
-    L.w0 = *reinterpret_cast<const uint4*>(wsrc[0] + off);
-    L.w1 = *reinterpret_cast<const uint4*>(wsrc[1] + off);
-    L.w2 = *reinterpret_cast<const uint4*>(wsrc[2] + off);
-    L.w3 = *reinterpret_cast<const uint4*>(wsrc[3] + off);
-    L.x0 = *reinterpret_cast<const uint4*>(xsrc[0] + off);
-    L.x1 = *reinterpret_cast<const uint4*>(xsrc[1] + off);
-    L.x2 = *reinterpret_cast<const uint4*>(xsrc[2] + off);
-    L.x3 = *reinterpret_cast<const uint4*>(xsrc[3] + off);
-    const size_t blk = static_cast<size_t>(8 * st + (full || sblk < 4 ? sblk : sblk - 4));
-    L.s0 = scale4(ws + blk * N, n0 + sr, N, w_dw);
-    L.s1 = scale4(xs + blk * M, m0 + sr, M, x_dw);
-    return L;
-  };
-  auto lstore = [&](auto buf_c, LoadRegs L) {
+  auto issue = [&](int st, auto buf_c) {
     constexpr int buf = decltype(buf_c)::value;
-    uint8_t* wd = &lds_c[buf][0] + ldst;
-    uint8_t* xd = &lds_c[buf][kTile * kMxRow] + ldst;
-    *reinterpret_cast<uint4*>(wd) = L.w0;
-    *reinterpret_cast<uint4*>(wd + 8 * kMxRow) = L.w1;
-    *reinterpret_cast<uint4*>(wd + 16 * kMxRow) = L.w2;
-    *reinterpret_cast<uint4*>(wd + 24 * kMxRow) = L.w3;
-    *reinterpret_cast<uint4*>(xd) = L.x0;
-    *reinterpret_cast<uint4*>(xd + 8 * kMxRow) = L.x1;
-    *reinterpret_cast<uint4*>(xd + 16 * kMxRow) = L.x2;
-    *reinterpret_cast<uint4*>(xd + 24 * kMxRow) = L.x3;
-    *reinterpret_cast<uint32_t*>(&lds_s[buf][0][sblk][sr]) = L.s0;
-    *reinterpret_cast<uint32_t*>(&lds_s[buf][1][sblk][sr]) = L.s1;
+    const int so = st * kMxStageB;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      lds_ptr_t dst = (lds_ptr_t)(&lds_c[buf][lds_op + (lrow - (lane >> 3) + 8 * j) * kMxdRowB]);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, dst, 16, vcode[j] + so, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int d0 = 128 * i + 64 * (wave & 1);          // first dword of this load
+      const int blk = 8 * st + ((d0 + lane) >> 5);
+      if (s_dw) {
+        lds_ptr_t sdst = (lds_ptr_t)(&lds_c[buf][lds_sc + 4 * d0]);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, sdst, 4, blk * rows + srow, 0, 0, 0);
+      } else {
+        uint32_t v = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v |= static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(rsc, blk * rows + min(srow + e, rows - 1), 0, 0))
+               << (8 * e);
+        *reinterpret_cast<uint32_t*>(&lds_c[buf][lds_sc + 4 * (d0 + lane)]) = v;
+      }
+    }
   };
 
   v16f acc[2][2];
@@ -829,24 +826,25 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_mxfp4(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[it][jt][r] = 0.f;
 
-  // 64-k substep s of a stage: code bytes 32s + 16h of the row, which are
-  // block 2s+h of the stage, and that block's scale byte
+  // 64-k substep s: logical chunk 2s + h of the row (block 2s + h of the
+  // stage), stored at chunk (2s + h) ^ (row % 8); row % 8 = l32 % 8
   auto compute = [&](auto buf_c, bool half) {
     constexpr int buf = decltype(buf_c)::value;
-    const uint8_t* wsc = &lds_s[buf][0][h][wn * 64 + l32];
-    const uint8_t* xsc = &lds_s[buf][1][h][wm * 64 + l32];
-    const uint8_t* wb = &lds_c[buf][0] + (wn * 64 + l32) * kMxRow + 16 * h;
-    const uint8_t* xb = &lds_c[buf][kTile * kMxRow] + (wm * 64 + l32) * kMxRow + 16 * h;
+    const uint8_t* wb = &lds_c[buf][0] + (wn * 64 + l32) * kMxdRowB;
+    const uint8_t* xb = &lds_c[buf][kMxdOp] + (wm * 64 + l32) * kMxdRowB;
+    const uint8_t* wsc = &lds_c[buf][2 * kMxdOp] + wn * 64 + l32;
+    const uint8_t* xsc = &lds_c[buf][2 * kMxdOp + 8 * kTile] + wm * 64 + l32;
     auto sub = [&](auto s_c) {
       constexpr int s = decltype(s_c)::value;
+      const int ch = ((2 * s + h) ^ (l32 & 7)) << 4;
       v4i a[2], b[2];
       uint32_t sa[2], sb[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        a[t] = *reinterpret_cast<const v4i*>(wb + t * 32 * kMxRow + 32 * s);
-        b[t] = *reinterpret_cast<const v4i*>(xb + t * 32 * kMxRow + 32 * s);
-        sa[t] = wsc[2 * s * kTile + t * 32];
-        sb[t] = xsc[2 * s * kTile + t * 32];
+        a[t] = *reinterpret_cast<const v4i*>(wb + t * 32 * kMxdRowB + ch);
+        b[t] = *reinterpret_cast<const v4i*>(xb + t * 32 * kMxdRowB + ch);
+        sa[t] = wsc[(2 * s + h) * kTile + t * 32];
+        sb[t] = xsc[(2 * s + h) * kTile + t * 32];
       }
 #pragma unroll
       for (int it = 0; it < 2; ++it)
@@ -862,16 +860,15 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_mxfp4(
     }
   };
 
-  LoadRegs ld = gload(0);
-  lstore(Slot<0>{}, ld);
-  if (S > 1) ld = gload(1);
+  const bool half_last = (K % kMxStage) != 0;
+  issue(0, Slot<0>{});
+  __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this wave's stage-0 data is in LDS
   __syncthreads();
-
   auto iteration = [&](int st, auto buf_c) {
     constexpr int buf = decltype(buf_c)::value;
-    if (st + 1 < S) lstore(Slot<1 - buf>{}, ld);
-    if (st + 2 < S) ld = gload(st + 2);
+    if (st + 1 < S) issue(st + 1, Slot<1 - buf>{});
     compute(buf_c, half_last && st == S - 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   };
   for (int st = 0; st < S; st += 2) {
@@ -883,7 +880,6 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_mxfp4(
                       wm, l32, h, tid, MlpOut{});
 }
 
-// ---------------------------------------------------------------------------
 // Kernel 2, INT4: 4-bit GEMM + per-group dequant + up projection + bias.
 //
 // Same tiling, two-slot pipeline and epilogue as the MXFP4 kernel: output
