@@ -1507,6 +1507,45 @@ hipError_t launch_unfused(const void* x, int M, int K, const float* sinv, const 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core ceiling, for the measurement only: every wave issues 8
+// independent v_mfma_scale_f32_32x32x64_f8f6f4 per iteration (FP8 operands,
+// or FP4 with PREC = SVDQ_MXFP4) on lane-dependent operand bits, so the rate
+// is that of dense MFMA issue at the clock this load sustains.  Two
+// workgroups of 4 waves per CU (2 waves per SIMD, as in the GEMMs).  out[b]
+// receives one sum per workgroup so nothing is dead code.
+// ---------------------------------------------------------------------------
+template <int PREC>
+__global__ __launch_bounds__(256, 2) void k_mfma_ceiling(int iters, float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t seed = 0x9E3779B9u * static_cast<uint32_t>(lane + 1 + threadIdx.x);
+  v8i a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    // FP8: bytes 0x08..0x37 (normal, moderate); FP4: any nibble
+    const uint32_t r = seed * (2u * i + 1u) ^ (seed >> 13);
+    a[i] = static_cast<int>(PREC == 1 ? r : (r & 0x37373737u) | 0x08080808u);
+    b[i] = static_cast<int>(PREC == 1 ? (r >> 3) | (r << 29) : ((r >> 3) & 0x37373737u) | 0x08080808u);
+  }
+  v16f c0 = {}, c1 = {}, c2 = {}, c3 = {}, c4 = {}, c5 = {}, c6 = {}, c7 = {};
+  constexpr int F = PREC == 1 ? 4 : 0;
+  for (int it = 0; it < iters; ++it) {
+    c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c0, F, F, 0, 0x70707070, 0, 0x70707070);
+    c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c1, F, F, 0, 0x70707070, 0, 0x70707070);
+    c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, a, c2, F, F, 0, 0x70707070, 0, 0x70707070);
+    c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, b, c3, F, F, 0, 0x70707070, 0, 0x70707070);
+    c4 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c4, F, F, 0, 0x71717171, 0, 0x70707070);
+    c5 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c5, F, F, 0, 0x71717171, 0, 0x70707070);
+    c6 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, a, c6, F, F, 0, 0x71717171, 0, 0x70707070);
+    c7 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, b, c7, F, F, 0, 0x71717171, 0, 0x70707070);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sum += c0[r] + c1[r] + c2[r] + c3[r] + c4[r] + c5[r] + c6[r] + c7[r];
+  sum += __shfl_xor(sum, 32);
+  if (threadIdx.x == 0) out[blockIdx.x] = sum;
+}
+
 }  // namespace
 
 extern "C" int svdq_launch_quantize_act_lora_down(const void* x, int M, int K, const float* smooth_inv,
@@ -1589,45 +1628,6 @@ extern "C" int svdq_launch_gemm_w4a16(const void* x, const uint8_t* wq, const vo
                      static_cast<const uint16_t*>(x), wq, static_cast<const uint16_t*>(ws),
                      static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), M, N, K);
   return static_cast<int>(hipGetLastError());
-}
-
-// ---------------------------------------------------------------------------
-// Matrix-core ceiling, for the measurement only: every wave issues 8
-// independent v_mfma_scale_f32_32x32x64_f8f6f4 per iteration (FP8 operands,
-// or FP4 with PREC = SVDQ_MXFP4) on lane-dependent operand bits, so the rate
-// is that of dense MFMA issue at the clock this load sustains.  Two
-// workgroups of 4 waves per CU (2 waves per SIMD, as in the GEMMs).  out[b]
-// receives one sum per workgroup so nothing is dead code.
-// ---------------------------------------------------------------------------
-template <int PREC>
-__global__ __launch_bounds__(256, 2) void k_mfma_ceiling(int iters, float* __restrict__ out) {
-  const int lane = threadIdx.x & 63;
-  const uint32_t seed = 0x9E3779B9u * static_cast<uint32_t>(lane + 1 + threadIdx.x);
-  v8i a, b;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    // FP8: bytes 0x08..0x37 (normal, moderate); FP4: any nibble
-    const uint32_t r = seed * (2u * i + 1u) ^ (seed >> 13);
-    a[i] = static_cast<int>(PREC == 1 ? r : (r & 0x37373737u) | 0x08080808u);
-    b[i] = static_cast<int>(PREC == 1 ? (r >> 3) | (r << 29) : ((r >> 3) & 0x37373737u) | 0x08080808u);
-  }
-  v16f c0 = {}, c1 = {}, c2 = {}, c3 = {}, c4 = {}, c5 = {}, c6 = {}, c7 = {};
-  constexpr int F = PREC == 1 ? 4 : 0;
-  for (int it = 0; it < iters; ++it) {
-    c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c0, F, F, 0, 0x70707070, 0, 0x70707070);
-    c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c1, F, F, 0, 0x70707070, 0, 0x70707070);
-    c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, a, c2, F, F, 0, 0x70707070, 0, 0x70707070);
-    c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, b, c3, F, F, 0, 0x70707070, 0, 0x70707070);
-    c4 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c4, F, F, 0, 0x71717171, 0, 0x70707070);
-    c5 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c5, F, F, 0, 0x71717171, 0, 0x70707070);
-    c6 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, a, c6, F, F, 0, 0x71717171, 0, 0x70707070);
-    c7 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, b, c7, F, F, 0, 0x71717171, 0, 0x70707070);
-  }
-  float sum = 0.f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) sum += c0[r] + c1[r] + c2[r] + c3[r] + c4[r] + c5[r] + c6[r] + c7[r];
-  sum += __shfl_xor(sum, 32);
-  if (threadIdx.x == 0) out[blockIdx.x] = sum;
 }
 
 extern "C" int svdq_launch_mfma_ceiling(int precision, int blocks, int iters, float* out, void* stream) {
