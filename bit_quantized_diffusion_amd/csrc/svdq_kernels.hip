@@ -415,6 +415,7 @@ __device__ __forceinline__ uint4 buffer_load_u4(__amdgpu_buffer_rsrc_t r, int vo
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 template <int S>
 struct Slot {
   static constexpr int value = S;
@@ -1029,18 +1030,16 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[it][jt][r] = 0.f;
 
-  // Both groups of a stage as one software pipeline over its 8 tile-groups
-  // (2 groups x 2 x 2 tiles): the MFMA of tile-group t+1 is issued before
-  // the dequant of tile-group t, and the second group's LDS operands are
-  // read while the first group computes.  sched_group_barrier states that
-  // order: left alone, the scheduler puts each dequant right behind the
-  // MFMA that feeds it and the VALU waits for the matrix core at every tile.
+  // Operands of group g (0, 1) of the stage in slot buf: FP8 bytes 64g +
+  // 32h of the row for lane half h, the E8M0 exponent bytes, and the rank-1
+  // operands of the scale outer product (below).
   struct Ops {
     v8i a0, a1, b0, b1;
     uint32_t ea0, ea1, eb0, eb1;
-    h2 mx0, mx1;
-    uint2 w00, w01, w02, w03, w10, w11, w12, w13;
+    h4 sa0, sa1, sb0, sb1;
   };
+  uint32_t hmask = h ? 0u : 0xFFFFu;     // k 0 of the outer product lives in lanes 0-31
+  asm volatile("" : "+v"(hmask));
   auto load_ops = [&](auto buf_c, auto g_c) {
     constexpr int buf = decltype(buf_c)::value;
     constexpr int g = decltype(g_c)::value;
@@ -1059,99 +1058,52 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
     o.ea1 = lds_e[buf][0][g][wn * 64 + 32 + l32];
     o.eb0 = lds_e[buf][1][g][wm * 64 + l32];
     o.eb1 = lds_e[buf][1][g][wm * 64 + 32 + l32];
-    const _Float16 m0x = lds_m[buf][1][g][wm * 64 + l32];
-    const _Float16 m1x = lds_m[buf][1][g][wm * 64 + 32 + l32];
-    o.mx0 = h2{m0x, m0x};
-    o.mx1 = h2{m1x, m1x};
-    const _Float16* mwp = &lds_m[buf][0][g][wn * 64 + 4 * h];
-    o.w00 = *reinterpret_cast<const uint2*>(mwp + 0);
-    o.w01 = *reinterpret_cast<const uint2*>(mwp + 8);
-    o.w02 = *reinterpret_cast<const uint2*>(mwp + 16);
-    o.w03 = *reinterpret_cast<const uint2*>(mwp + 24);
-    o.w10 = *reinterpret_cast<const uint2*>(mwp + 32);
-    o.w11 = *reinterpret_cast<const uint2*>(mwp + 40);
-    o.w12 = *reinterpret_cast<const uint2*>(mwp + 48);
-    o.w13 = *reinterpret_cast<const uint2*>(mwp + 56);
+    const uint16_t* mw16 = reinterpret_cast<const uint16_t*>(&lds_m[buf][0][g][0]);
+    const uint16_t* mx16 = reinterpret_cast<const uint16_t*>(&lds_m[buf][1][g][0]);
+    auto op = [&](uint32_t v) { return __builtin_bit_cast(h4, make_uint2(v & hmask, 0u)); };
+    o.sa0 = op(mw16[wn * 64 + l32]);
+    o.sa1 = op(mw16[wn * 64 + 32 + l32]);
+    o.sb0 = op(mx16[wm * 64 + l32]);
+    o.sb1 = op(mx16[wm * 64 + 32 + l32]);
     return o;
   };
+  // tile-group t = 2 it + jt: the group's partial P of W tile it and X
+  // tile jt, times 2^(e_w + e_x) (exact)
   auto mf2 = [&](const Ops& o, auto t_c) {
     constexpr int t = decltype(t_c)::value;
     constexpr int it = t >> 1, jt = t & 1;
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(it ? o.a1 : o.a0, jt ? o.b1 : o.b0, v16f{}, 0, 0, 0,
                                                            it ? o.ea1 : o.ea0, 0, jt ? o.eb1 : o.eb0);
   };
+  // Dequant of tile-group t.  The products m_w(n) m_x(m) of the scale
+  // significands form a rank-1 32 x 32 matrix: v_mfma_f32_32x32x8_f16 with
+  // k 0 holding m_w (A, lanes 0-31) and m_x (B) and k 1..7 zero returns it
+  // exactly in fp32, in the accumulator layout of P, so that the dequant is
+  // one fp32 FMA per element on the VALU.
+  const v16f zero16 = {};
   auto dq2 = [&](const Ops& o, auto t_c, const v16f& p) {
     constexpr int t = decltype(t_c)::value;
     constexpr int it = t >> 1, jt = t & 1;
-    const h2 mx = jt ? o.mx1 : o.mx0;
-    const uint2 mw[4] = {it ? o.w10 : o.w00, it ? o.w11 : o.w01, it ? o.w12 : o.w02, it ? o.w13 : o.w03};
+    const v16f c = __builtin_amdgcn_mfma_f32_32x32x8f16(it ? o.sa1 : o.sa0, jt ? o.sb1 : o.sb0, zero16, 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const h2 s01 = __builtin_bit_cast(h2, mw[j].x) * mx;
-      const h2 s23 = __builtin_bit_cast(h2, mw[j].y) * mx;
-      acc[it][jt][4 * j + 0] = __builtin_fmaf(p[4 * j + 0], static_cast<float>(s01[0]), acc[it][jt][4 * j + 0]);
-      acc[it][jt][4 * j + 1] = __builtin_fmaf(p[4 * j + 1], static_cast<float>(s01[1]), acc[it][jt][4 * j + 1]);
-      acc[it][jt][4 * j + 2] = __builtin_fmaf(p[4 * j + 2], static_cast<float>(s23[0]), acc[it][jt][4 * j + 2]);
-      acc[it][jt][4 * j + 3] = __builtin_fmaf(p[4 * j + 3], static_cast<float>(s23[1]), acc[it][jt][4 * j + 3]);
-    }
+    for (int r = 0; r < 16; ++r) acc[it][jt][r] = __builtin_fmaf(p[r], c[r], acc[it][jt][r]);
   };
   using I0 = Slot<0>;
   using I1 = Slot<1>;
   using I2 = Slot<2>;
   using I3 = Slot<3>;
-  // pin: the MFMA that produced pn is issued before the dequant that
-  // updates acc[it][jt] (the asm reads pn's registers only nominally)
-  auto pin = [](v16f& pn, v16f& a) { asm volatile("" : "+v"(pn), "+v"(a)); };
-  auto two_groups = [&](auto buf_c) {
-    const Ops o0 = load_ops(buf_c, I0{});
-    v16f pa = mf2(o0, I0{});
-    v16f pb = mf2(o0, I1{});
-    pin(pb, acc[0][0]);
-    dq2(o0, I0{}, pa);
-    pa = mf2(o0, I2{});
-    pin(pa, acc[0][1]);
-    dq2(o0, I1{}, pb);
-    pb = mf2(o0, I3{});
-    pin(pb, acc[1][0]);
-    const Ops o1 = load_ops(buf_c, I1{});
-    dq2(o0, I2{}, pa);
-    pa = mf2(o1, I0{});
-    pin(pa, acc[1][1]);
-    dq2(o0, I3{}, pb);
-    pb = mf2(o1, I1{});
-    pin(pb, acc[0][0]);
-    dq2(o1, I0{}, pa);
-    pa = mf2(o1, I2{});
-    pin(pa, acc[0][1]);
-    dq2(o1, I1{}, pb);
-    pb = mf2(o1, I3{});
-    pin(pb, acc[1][0]);
-    dq2(o1, I2{}, pa);
-    dq2(o1, I3{}, pb);
-  };
 
-  // group g of the stage: FP8 bytes 64g + 32h of the row for lane half h
+  // A stage (one group on an odd-G last stage) as one software pipeline
+  // over its tile-groups: the MFMA of tile-group t+1 is issued before the
+  // dequant of tile-group t; the second group's operands are read while the
+  // first group computes.  DEBUG: unit scales, and the exact integer
+  // partial of every group written for the window instead.
   auto compute = [&](auto buf_c, bool one, int g0) {
-    constexpr int buf = decltype(buf_c)::value;
-    auto group = [&](auto g_c) {
-      constexpr int g = decltype(g_c)::value;
-      v8i a[2], b[2];
-      uint32_t ea[2], eb[2];
-      h2 mx2[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int8_t* wr = &lds_c[buf][0] + (wn * 64 + t * 32 + l32) * kI4Row + 64 * g + 32 * h;
-        const int8_t* xr = &lds_c[buf][kTile * kI4Row] + (wm * 64 + t * 32 + l32) * kI4Row + 64 * g + 32 * h;
-        a[t] = __builtin_shufflevector(*reinterpret_cast<const v4i*>(wr), *reinterpret_cast<const v4i*>(wr + 16), 0, 1,
-                                       2, 3, 4, 5, 6, 7);
-        b[t] = __builtin_shufflevector(*reinterpret_cast<const v4i*>(xr), *reinterpret_cast<const v4i*>(xr + 16), 0, 1,
-                                       2, 3, 4, 5, 6, 7);
-        ea[t] = lds_e[buf][0][g][wn * 64 + t * 32 + l32];
-        eb[t] = lds_e[buf][1][g][wm * 64 + t * 32 + l32];
-        const _Float16 mx = lds_m[buf][1][g][wm * 64 + t * 32 + l32];
-        mx2[t] = h2{mx, mx};
-      }
-      if constexpr (DEBUG) {
+    if constexpr (DEBUG) {
+      auto group = [&](auto g_c) {
+        constexpr int g = decltype(g_c)::value;
+        const Ops o = load_ops(buf_c, g_c);
+        const v8i a[2] = {o.a0, o.a1}, b[2] = {o.b0, o.b1};
 #pragma unroll
         for (int it = 0; it < 2; ++it)
 #pragma unroll
@@ -1173,50 +1125,34 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
                 dbg[(static_cast<size_t>(m - win_m0) * win_nt + (n - win_n0)) * G + g0 + g] = pi[r];
             }
           }
+      };
+      group(I0{});
+      if (!one) group(I1{});
+    } else {
+      const Ops o0 = load_ops(buf_c, I0{});
+      v16f pa = mf2(o0, I0{});
+      v16f pb = mf2(o0, I1{});
+      dq2(o0, I0{}, pa);
+      pa = mf2(o0, I2{});
+      dq2(o0, I1{}, pb);
+      pb = mf2(o0, I3{});
+      if (one) {
+        dq2(o0, I2{}, pa);
+        dq2(o0, I3{}, pb);
         return;
       }
-      // significands of the 4 consecutive W rows of lane elements 4j..4j+3
-      uint2 mw[2][4];
-#pragma unroll
-      for (int it = 0; it < 2; ++it)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          mw[it][j] = *reinterpret_cast<const uint2*>(&lds_m[buf][0][g][wn * 64 + it * 32 + 8 * j + 4 * h]);
-      auto mf = [&](int t) {
-        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[t >> 1], b[t & 1], v16f{}, 0, 0, 0, ea[t >> 1], 0,
-                                                               eb[t & 1]);
-      };
-      auto dq = [&](int t, const v16f& p) {
-        const int it = t >> 1, jt = t & 1;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const h2 s01 = __builtin_bit_cast(h2, mw[it][j].x) * mx2[jt];
-          const h2 s23 = __builtin_bit_cast(h2, mw[it][j].y) * mx2[jt];
-          acc[it][jt][4 * j + 0] = __builtin_fmaf(p[4 * j + 0], static_cast<float>(s01[0]), acc[it][jt][4 * j + 0]);
-          acc[it][jt][4 * j + 1] = __builtin_fmaf(p[4 * j + 1], static_cast<float>(s01[1]), acc[it][jt][4 * j + 1]);
-          acc[it][jt][4 * j + 2] = __builtin_fmaf(p[4 * j + 2], static_cast<float>(s23[0]), acc[it][jt][4 * j + 2]);
-          acc[it][jt][4 * j + 3] = __builtin_fmaf(p[4 * j + 3], static_cast<float>(s23[1]), acc[it][jt][4 * j + 3]);
-        }
-      };
-      // software pipeline: the MFMA of tile t+1 is issued before the
-      // dequant of tile t, so that the matrix core and the VALU overlap
-      v16f p0 = mf(0);
-      v16f p1 = mf(1);
-      dq(0, p0);
-      p0 = mf(2);
-      dq(1, p1);
-      p1 = mf(3);
-      dq(2, p0);
-      dq(3, p1);
-    };
-    if constexpr (!DEBUG) {
-      if (!one) {
-        two_groups(buf_c);
-        return;
-      }
+      const Ops o1 = load_ops(buf_c, I1{});
+      dq2(o0, I2{}, pa);
+      pa = mf2(o1, I0{});
+      dq2(o0, I3{}, pb);
+      pb = mf2(o1, I1{});
+      dq2(o1, I0{}, pa);
+      pa = mf2(o1, I2{});
+      dq2(o1, I1{}, pb);
+      pb = mf2(o1, I3{});
+      dq2(o1, I2{}, pa);
+      dq2(o1, I3{}, pb);
     }
-    group(Slot<0>{});
-    if (!one) group(Slot<1>{});
   };
 
   LoadRegs ld = gload(0);
