@@ -626,13 +626,45 @@ __device__ __forceinline__ void mlp_tail(uint16_t* __restrict__ stg, int M, int 
 // columns (tile-local: a group lies inside the 128-column tile), and its
 // partial down projection x^2 . L1_2 over the tile's 128 columns, summed
 // into lact2 with fp32 atomics (lact2 cleared beforehand).
-template <int EPI>
+// UPL: rank 32, and the tile's lora_act rows (128 x 32 fp32, 128-byte rows,
+// 16-byte chunk c of row r at chunk c ^ (r % 8)) and L2 rows (128 x 32 bf16
+// at byte 16384, 64-byte rows, chunk c of row r at c ^ ((r / 4) % 4)) are
+// already in LDS at upl.
+template <int EPI, bool UPL = false>
 __device__ __forceinline__ void epilogue_tile128(v16f (&acc)[2][2], uint16_t* __restrict__ stg,
                                                  const float* __restrict__ lact, const uint16_t* __restrict__ lup,
                                                  const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M,
                                                  int N, int rank, int n0, int m0, int wn, int wm, int l32, int h,
-                                                 int tid, const MlpOut& mo) {
-  for (int c0 = 0; c0 < rank; c0 += 16) {
+                                                 int tid, const MlpOut& mo, const uint8_t* upl = nullptr) {
+  if constexpr (UPL) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      v4i ub[2], ua[2];
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        const int r = wm * 64 + jt * 32 + l32;
+        const uint8_t* row = upl + r * 128;
+        const float4 f0 = *reinterpret_cast<const float4*>(row + (((4 * c + 2 * h) ^ (r & 7)) << 4));
+        const float4 f1 = *reinterpret_cast<const float4*>(row + (((4 * c + 2 * h + 1) ^ (r & 7)) << 4));
+        ub[jt] = m0 + r < M ? v4i{static_cast<int>(pack_bf16_rne(f0.x, f0.y)), static_cast<int>(pack_bf16_rne(f0.z, f0.w)),
+                                  static_cast<int>(pack_bf16_rne(f1.x, f1.y)), static_cast<int>(pack_bf16_rne(f1.z, f1.w))}
+                            : v4i{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int r = wn * 64 + it * 32 + l32;
+        ua[it] = n0 + r < N ? *reinterpret_cast<const v4i*>(upl + 16384 + r * 64 + (((2 * c + h) ^ ((r >> 2) & 3)) << 4))
+                            : v4i{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+          acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ua[it]),
+                                                                __builtin_bit_cast(v8bf, ub[jt]), acc[it][jt], 0, 0, 0);
+    }
+  }
+  for (int c0 = 0; c0 < (UPL ? 0 : rank); c0 += 16) {
     const int j = c0 + 8 * h;
     v4i ub[2], ua[2];
 #pragma unroll
@@ -862,12 +894,37 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_mxfp4(
   };
 
   const bool half_last = (K % kMxStage) != 0;
+  // Rank 32: during the last stage the tile's lora_act rows (16 KB) and L2
+  // rows (8 KB) are loaded straight into the slot that stage does not use
+  // (layout of epilogue_tile128's UPL mode; rows past the edge read zero),
+  // and the output is staged in the other slot.  Wave w moves lora_act
+  // rows 32 w .. + 31 (four loads of 8 rows) and L2 rows 32 w .. + 31 (two
+  // loads of 16 rows).
+  const bool upl = rank == 32;
+  auto issue_up = [&](auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(lact + static_cast<size_t>(m0) * 32, static_cast<size_t>(M - m0) * 128);
+    const __amdgpu_buffer_rsrc_t ru = make_rsrc(lup + static_cast<size_t>(n0) * 32, static_cast<size_t>(N - n0) * 64);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int blk = 4 * wave + j, r = 8 * blk + (lane >> 3);
+      lds_ptr_t dst = (lds_ptr_t)(&lds_c[buf][blk * 1024]);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, r * 128 + (((lane & 7) ^ (r & 7)) << 4), 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int blk = 2 * wave + j, r = 16 * blk + (lane >> 2);
+      lds_ptr_t dst = (lds_ptr_t)(&lds_c[buf][16384 + blk * 1024]);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, dst, 16, r * 64 + (((lane & 3) ^ ((r >> 2) & 3)) << 4), 0, 0, 0);
+    }
+  };
   issue(0, Slot<0>{});
   __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this wave's stage-0 data is in LDS
   __syncthreads();
   auto iteration = [&](int st, auto buf_c) {
     constexpr int buf = decltype(buf_c)::value;
     if (st + 1 < S) issue(st + 1, Slot<1 - buf>{});
+    else if (upl) issue_up(Slot<1 - buf>{});
     compute(buf_c, half_last && st == S - 1);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
@@ -877,8 +934,13 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_mxfp4(
     if (st + 1 < S) iteration(st + 1, Slot<1>{});
   }
 
-  epilogue_tile128<0>(acc, reinterpret_cast<uint16_t*>(&lds_c[0][0]), lact, lup, bias, y, M, N, rank, n0, m0, wn,
-                      wm, l32, h, tid, MlpOut{});
+  const int last = (S - 1) & 1;
+  if (upl)
+    epilogue_tile128<0, true>(acc, reinterpret_cast<uint16_t*>(&lds_c[last][0]), lact, lup, bias, y, M, N, rank, n0,
+                              m0, wn, wm, l32, h, tid, MlpOut{}, &lds_c[1 - last][0]);
+  else
+    epilogue_tile128<0>(acc, reinterpret_cast<uint16_t*>(&lds_c[0][0]), lact, lup, bias, y, M, N, rank, n0, m0, wn,
+                        wm, l32, h, tid, MlpOut{});
 }
 
 // Kernel 2, INT4: 4-bit GEMM + per-group dequant + up projection + bias.
@@ -891,8 +953,9 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_mxfp4(
 // so that v_mfma_scale_f32_32x32x64_f8f6f4 returns the group's exact integer
 // partial P scaled by 2^(e_w + e_x) (exponents of the two scales applied as
 // E8M0 block scales, with 2^18 on the W side to cancel the code encoding).
-// The scale significands in [0.5, 1) multiply in packed fp16 and
-// v_fma_mix_f32 adds P' * (m_w m_x) into the fp32 accumulators.
+// The products of the scale significands (in [0.5, 1)) come from a rank-1
+// v_mfma_f32_32x32x8_f16, exact in fp32 and in P's layout, and one fp32 FMA
+// per element adds P' * (m_w m_x) into the accumulators.
 //
 // DEBUG = true is a test hook on the same loader, LDS layout and MFMA path:
 // unit scales, and the exact integer partial of every K-group written for a
