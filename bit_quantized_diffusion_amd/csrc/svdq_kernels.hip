@@ -772,9 +772,35 @@ __device__ __forceinline__ v16f mfma_fp4(const v4i& a, const v4i& b, const v16f&
 constexpr int kMxdRowB = 128;                      // LDS bytes per row and stage (no padding)
 constexpr int kMxdOp = kTile * kMxdRowB;           // one operand's rows
 constexpr int kMxdSlot = 2 * kMxdOp + 2 * 8 * kTile;   // W rows, X rows, then scales [W|X][block][row]
-static_assert(2 * kMxdSlot >= kTile * kMxYRow * 2, "output staging fits in the ring");
+static_assert(kMxdSlot >= kTile * kMxYRow * 2, "output staging fits in one slot of the ring");
+static_assert(kMxdSlot >= 16384 + 8192, "rank-32 up-projection operands fit in one slot");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Rank 32: a tile's lora_act rows m0 .. +127 (fp32, 16 KB) and L2 rows
+// n0 .. +127 (bf16, 8 KB) straight from memory into LDS at dst, in the
+// layout of epilogue_tile128's UPL mode; rows past the edge read zero.
+// Wave w (wave-uniform) moves lora_act rows 32 w .. +31 (four loads of 8
+// rows) and L2 rows 32 w .. +31 (two loads of 16 rows); the caller waits
+// (vmcnt) and synchronises before the epilogue reads them.
+__device__ __forceinline__ void upl_issue(uint8_t* dst, const float* __restrict__ lact,
+                                          const uint16_t* __restrict__ lup, int M, int N, int m0, int n0, int wave,
+                                          int lane) {
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(lact + static_cast<size_t>(m0) * 32, static_cast<size_t>(M - m0) * 128);
+  const __amdgpu_buffer_rsrc_t ru = make_rsrc(lup + static_cast<size_t>(n0) * 32, static_cast<size_t>(N - n0) * 64);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int blk = 4 * wave + j, r = 8 * blk + (lane >> 3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(dst + blk * 1024), 16,
+                                             r * 128 + (((lane & 7) ^ (r & 7)) << 4), 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int blk = 2 * wave + j, r = 16 * blk + (lane >> 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (lds_ptr_t)(dst + 16384 + blk * 1024), 16,
+                                             r * 64 + (((lane & 3) ^ ((r >> 2) & 3)) << 4), 0, 0, 0);
+  }
+}
 
 __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_mxfp4(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
@@ -894,29 +920,12 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_mxfp4(
   };
 
   const bool half_last = (K % kMxStage) != 0;
-  // Rank 32: during the last stage the tile's lora_act rows (16 KB) and L2
-  // rows (8 KB) are loaded straight into the slot that stage does not use
-  // (layout of epilogue_tile128's UPL mode; rows past the edge read zero),
-  // and the output is staged in the other slot.  Wave w moves lora_act
-  // rows 32 w .. + 31 (four loads of 8 rows) and L2 rows 32 w .. + 31 (two
-  // loads of 16 rows).
+  // Rank 32: during the last stage the tile's up-projection operands come
+  // straight into the slot that stage does not use (upl_issue), and the
+  // output is staged in the other slot.
   const bool upl = rank == 32;
   auto issue_up = [&](auto buf_c) {
-    constexpr int buf = decltype(buf_c)::value;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(lact + static_cast<size_t>(m0) * 32, static_cast<size_t>(M - m0) * 128);
-    const __amdgpu_buffer_rsrc_t ru = make_rsrc(lup + static_cast<size_t>(n0) * 32, static_cast<size_t>(N - n0) * 64);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int blk = 4 * wave + j, r = 8 * blk + (lane >> 3);
-      lds_ptr_t dst = (lds_ptr_t)(&lds_c[buf][blk * 1024]);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, r * 128 + (((lane & 7) ^ (r & 7)) << 4), 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int blk = 2 * wave + j, r = 16 * blk + (lane >> 2);
-      lds_ptr_t dst = (lds_ptr_t)(&lds_c[buf][16384 + blk * 1024]);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, dst, 16, r * 64 + (((lane & 3) ^ ((r >> 2) & 3)) << 4), 0, 0, 0);
-    }
+    upl_issue(&lds_c[decltype(buf_c)::value][0], lact, lup, M, N, m0, n0, wave, lane);
   };
   issue(0, Slot<0>{});
   __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this wave's stage-0 data is in LDS
