@@ -133,6 +133,12 @@ __global__ __launch_bounds__(256) void k1_quant_down_int4(
 #pragma unroll
   for (int t = 0; t < (RT > 0 ? RT : 1); ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // the first step's X is requested before the LDS staging below, so that
+  // its latency overlaps that of the staging loads and barriers
+  uint4 xn[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) xn[c] = *reinterpret_cast<const uint4*>(xr + kof(k_begin, c));
+
   // smooth_inv is read by every step of every wave: stage the slice in LDS
   for (int i = threadIdx.x; i < (k_end - k_begin) / 4; i += blockDim.x)
     reinterpret_cast<float4*>(lds_sinv)[i] = reinterpret_cast<const float4*>(sinv + k_begin)[i];
@@ -176,9 +182,6 @@ __global__ __launch_bounds__(256) void k1_quant_down_int4(
     __syncthreads();
   }
 
-  uint4 xn[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) xn[c] = *reinterpret_cast<const uint4*>(xr + kof(k_begin, c));
   auto load_l1 = [&](v4i (&dst)[4][TB], int kbase, int t0) {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
