@@ -1150,16 +1150,20 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(it ? o.a1 : o.a0, jt ? o.b1 : o.b0, v16f{}, 0, 0, 0,
                                                            it ? o.ea1 : o.ea0, 0, jt ? o.eb1 : o.eb0);
   };
-  // Dequant of tile-group t.  The products m_w(n) m_x(m) of the scale
-  // significands form a rank-1 32 x 32 matrix: v_mfma_f32_32x32x8_f16 with
-  // k 0 holding m_w (A, lanes 0-31) and m_x (B) and k 1..7 zero returns it
-  // exactly in fp32, in the accumulator layout of P, so that the dequant is
-  // one fp32 FMA per element on the VALU.
+  // Scale outer product of tile-group t.  The products m_w(n) m_x(m) of
+  // the scale significands form a rank-1 32 x 32 matrix:
+  // v_mfma_f32_32x32x8_f16 with k 0 holding m_w (A, lanes 0-31) and m_x (B)
+  // and k 1..7 zero returns it exactly in fp32, in the accumulator layout of
+  // P, so that the dequant (dqc) is one fp32 FMA per element on the VALU.
   const v16f zero16 = {};
-  auto dq2 = [&](const Ops& o, auto t_c, const v16f& p) {
+  auto rk = [&](const Ops& o, auto t_c) {
     constexpr int t = decltype(t_c)::value;
     constexpr int it = t >> 1, jt = t & 1;
-    const v16f c = __builtin_amdgcn_mfma_f32_32x32x8f16(it ? o.sa1 : o.sa0, jt ? o.sb1 : o.sb0, zero16, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x8f16(it ? o.sa1 : o.sa0, jt ? o.sb1 : o.sb0, zero16, 0, 0, 0);
+  };
+  auto dqc = [&](auto t_c, const v16f& p, const v16f& c) {
+    constexpr int t = decltype(t_c)::value;
+    constexpr int it = t >> 1, jt = t & 1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[it][jt][r] = __builtin_fmaf(p[r], c[r], acc[it][jt][r]);
   };
@@ -1169,9 +1173,10 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   using I3 = Slot<3>;
 
   // A stage (one group on an odd-G last stage) as one software pipeline
-  // over its tile-groups: the MFMA of tile-group t+1 is issued before the
-  // dequant of tile-group t; the second group's operands are read while the
-  // first group computes.  DEBUG: unit scales, and the exact integer
+  // over its tile-groups: both MFMAs of tile-group t+1 (the FP8 product and
+  // the scale outer product) are issued before the dequant of tile-group t,
+  // so the FMAs find their operands done; the second group's operands are
+  // read while the first group computes.  DEBUG: unit scales, and the exact integer
   // partial of every group written for the window instead.
   auto compute = [&](auto buf_c, bool one, int g0) {
     if constexpr (DEBUG) {
@@ -1207,26 +1212,34 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
       const Ops o0 = load_ops(buf_c, I0{});
       v16f pa = mf2(o0, I0{});
       v16f pb = mf2(o0, I1{});
-      dq2(o0, I0{}, pa);
+      v16f ca = rk(o0, I0{});
+      v16f cb = rk(o0, I1{});
+      dqc(I0{}, pa, ca);
       pa = mf2(o0, I2{});
-      dq2(o0, I1{}, pb);
+      ca = rk(o0, I2{});
+      dqc(I1{}, pb, cb);
       pb = mf2(o0, I3{});
+      cb = rk(o0, I3{});
       if (one) {
-        dq2(o0, I2{}, pa);
-        dq2(o0, I3{}, pb);
+        dqc(I2{}, pa, ca);
+        dqc(I3{}, pb, cb);
         return;
       }
       const Ops o1 = load_ops(buf_c, I1{});
-      dq2(o0, I2{}, pa);
+      dqc(I2{}, pa, ca);
       pa = mf2(o1, I0{});
-      dq2(o0, I3{}, pb);
+      ca = rk(o1, I0{});
+      dqc(I3{}, pb, cb);
       pb = mf2(o1, I1{});
-      dq2(o1, I0{}, pa);
+      cb = rk(o1, I1{});
+      dqc(I0{}, pa, ca);
       pa = mf2(o1, I2{});
-      dq2(o1, I1{}, pb);
+      ca = rk(o1, I2{});
+      dqc(I1{}, pb, cb);
       pb = mf2(o1, I3{});
-      dq2(o1, I2{}, pa);
-      dq2(o1, I3{}, pb);
+      cb = rk(o1, I3{});
+      dqc(I2{}, pa, ca);
+      dqc(I3{}, pb, cb);
     }
   };
 
