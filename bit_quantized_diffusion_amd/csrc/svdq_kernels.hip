@@ -1178,6 +1178,13 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   // so the FMAs find their operands done; the second group's operands are
   // read while the first group computes.  DEBUG: unit scales, and the exact integer
   // partial of every group written for the window instead.
+  // the stage's last two tile-groups (it = 1) leave compute with their
+  // MFMAs in flight; their dequant (finish) runs after the stage barrier
+  v16f pa, pb, ca, cb;
+  auto finish = [&]() {
+    dqc(I2{}, pa, ca);
+    dqc(I3{}, pb, cb);
+  };
   auto compute = [&](auto buf_c, bool one, int g0) {
     if constexpr (DEBUG) {
       auto group = [&](auto g_c) {
@@ -1210,21 +1217,17 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
       if (!one) group(I1{});
     } else {
       const Ops o0 = load_ops(buf_c, I0{});
-      v16f pa = mf2(o0, I0{});
-      v16f pb = mf2(o0, I1{});
-      v16f ca = rk(o0, I0{});
-      v16f cb = rk(o0, I1{});
+      pa = mf2(o0, I0{});
+      pb = mf2(o0, I1{});
+      ca = rk(o0, I0{});
+      cb = rk(o0, I1{});
       dqc(I0{}, pa, ca);
       pa = mf2(o0, I2{});
       ca = rk(o0, I2{});
       dqc(I1{}, pb, cb);
       pb = mf2(o0, I3{});
       cb = rk(o0, I3{});
-      if (one) {
-        dqc(I2{}, pa, ca);
-        dqc(I3{}, pb, cb);
-        return;
-      }
+      if (one) return;
       const Ops o1 = load_ops(buf_c, I1{});
       dqc(I2{}, pa, ca);
       pa = mf2(o1, I0{});
@@ -1238,8 +1241,6 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
       dqc(I1{}, pb, cb);
       pb = mf2(o1, I3{});
       cb = rk(o1, I3{});
-      dqc(I2{}, pa, ca);
-      dqc(I3{}, pb, cb);
     }
   };
 
@@ -1251,6 +1252,8 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   auto iteration = [&](int st, auto buf_c) {
     constexpr int buf = decltype(buf_c)::value;
     if (st + 1 < S) lstore(Slot<1 - buf>{}, ld);
+    if constexpr (!DEBUG)
+      if (st > 0) finish();
     if (st + 2 < S) ld = gload(st + 2);
     compute(buf_c, 2 * st + 1 >= G, 2 * st);
     __syncthreads();
@@ -1260,6 +1263,7 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
     if (st + 1 < S) iteration(st + 1, Slot<1>{});
   }
 
+  if constexpr (!DEBUG) finish();
   if constexpr (!DEBUG)
     epilogue_tile128<EPI>(acc, reinterpret_cast<uint16_t*>(&lds_c[0][0]), lact, lup, bias, y, M, N, rank, n0, m0, wn,
                           wm, l32, h, tid, mo);
