@@ -986,10 +986,10 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N, int K, int rank,
     int win_m0, int win_n0, int win_mt, int win_nt, int32_t* __restrict__ dbg, MlpOut mo) {
   __shared__ __attribute__((aligned(16))) int8_t lds_c[2][kI4Slot];
-  // per slot, operand (0 = W, 1 = X), group of the stage and row: the E8M0
-  // exponent byte of the scale and its fp16 significand
-  __shared__ __attribute__((aligned(16))) uint8_t lds_e[2][2][2][kTile];
-  __shared__ __attribute__((aligned(16))) _Float16 lds_m[2][2][2][kTile];
+  // per slot, operand (0 = W, 1 = X), group of the stage and row: the fp16
+  // significand of the scale (bits 0-15) and its E8M0 exponent byte (bits
+  // 16-23)
+  __shared__ __attribute__((aligned(16))) uint32_t lds_s[2][2][2][kTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1093,8 +1093,9 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
       eb[i] = static_cast<uint32_t>(__builtin_amdgcn_frexp_exph(sv) + (s_is_w ? 127 + 18 : 127)) & 0xFFu;
       sm[i] = __builtin_amdgcn_frexp_manth(sv);
     }
-    *reinterpret_cast<uint16_t*>(&lds_e[buf][s_is_w ? 0 : 1][sg][sr]) = static_cast<uint16_t>(eb[0] | (eb[1] << 8));
-    *reinterpret_cast<h2*>(&lds_m[buf][s_is_w ? 0 : 1][sg][sr]) = h2{sm[0], sm[1]};
+    *reinterpret_cast<uint2*>(&lds_s[buf][s_is_w ? 0 : 1][sg][sr]) =
+        make_uint2(static_cast<uint32_t>(__builtin_bit_cast(uint16_t, sm[0])) | (eb[0] << 16),
+                   static_cast<uint32_t>(__builtin_bit_cast(uint16_t, sm[1])) | (eb[1] << 16));
   };
 
   v16f acc[2][2];
@@ -1129,17 +1130,17 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
     o.a1 = rd(wr + 32 * kI4Row);
     o.b0 = rd(xr);
     o.b1 = rd(xr + 32 * kI4Row);
-    o.ea0 = lds_e[buf][0][g][wn * 64 + l32];
-    o.ea1 = lds_e[buf][0][g][wn * 64 + 32 + l32];
-    o.eb0 = lds_e[buf][1][g][wm * 64 + l32];
-    o.eb1 = lds_e[buf][1][g][wm * 64 + 32 + l32];
-    const uint16_t* mw16 = reinterpret_cast<const uint16_t*>(&lds_m[buf][0][g][0]);
-    const uint16_t* mx16 = reinterpret_cast<const uint16_t*>(&lds_m[buf][1][g][0]);
+    // one word per row: the exponent byte goes to the MFMA as byte 2
+    // (op_sel 2), the significand (bits 0-15) to the outer product
+    o.ea0 = lds_s[buf][0][g][wn * 64 + l32];
+    o.ea1 = lds_s[buf][0][g][wn * 64 + 32 + l32];
+    o.eb0 = lds_s[buf][1][g][wm * 64 + l32];
+    o.eb1 = lds_s[buf][1][g][wm * 64 + 32 + l32];
     auto op = [&](uint32_t v) { return __builtin_bit_cast(h4, make_uint2(v & hmask, 0u)); };
-    o.sa0 = op(mw16[wn * 64 + l32]);
-    o.sa1 = op(mw16[wn * 64 + 32 + l32]);
-    o.sb0 = op(mx16[wm * 64 + l32]);
-    o.sb1 = op(mx16[wm * 64 + 32 + l32]);
+    o.sa0 = op(o.ea0);
+    o.sa1 = op(o.ea1);
+    o.sb0 = op(o.eb0);
+    o.sb1 = op(o.eb1);
     return o;
   };
   // tile-group t = 2 it + jt: the group's partial P of W tile it and X
@@ -1147,8 +1148,8 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   auto mf2 = [&](const Ops& o, auto t_c) {
     constexpr int t = decltype(t_c)::value;
     constexpr int it = t >> 1, jt = t & 1;
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(it ? o.a1 : o.a0, jt ? o.b1 : o.b0, v16f{}, 0, 0, 0,
-                                                           it ? o.ea1 : o.ea0, 0, jt ? o.eb1 : o.eb0);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(it ? o.a1 : o.a0, jt ? o.b1 : o.b0, v16f{}, 0, 0, 2,
+                                                           it ? o.ea1 : o.ea0, 2, jt ? o.eb1 : o.eb0);
   };
   // Scale outer product of tile-group t.  The products m_w(n) m_x(m) of
   // the scale significands form a rank-1 32 x 32 matrix:
