@@ -1075,7 +1075,9 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   // (v_frexp_mant_f16, v_frexp_exp_i16_f16, subnormals included): 2^e is
   // applied exactly by the matrix core as an E8M0 block scale, m is an
   // exact fp16.  W rows carry an extra 2^18 that cancels the 2^-18 of the
-  // FP8 code encoding.  s == 0 gives m = 0; its codes are zero too.
+  // FP8 code encoding; X rows carry 2^-1 that cancels the doubled outer
+  // product of the significands.  s == 0 gives m = 0; its codes are zero
+  // too.
   auto lstore = [&](auto buf_c, LoadRegs L) {
     constexpr int buf = decltype(buf_c)::value;
     int8_t* wd = &lds_c[buf][0] + ldst;
@@ -1090,7 +1092,7 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const _Float16 sv = __builtin_bit_cast(_Float16, static_cast<uint16_t>(L.s >> (16 * i)));
-      eb[i] = static_cast<uint32_t>(__builtin_amdgcn_frexp_exph(sv) + (s_is_w ? 127 + 18 : 127)) & 0xFFu;
+      eb[i] = static_cast<uint32_t>(__builtin_amdgcn_frexp_exph(sv) + (s_is_w ? 127 + 18 : 127 - 1)) & 0xFFu;
       sm[i] = __builtin_amdgcn_frexp_manth(sv);
     }
     *reinterpret_cast<uint2*>(&lds_s[buf][s_is_w ? 0 : 1][sg][sr]) =
@@ -1114,8 +1116,6 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
     uint32_t ea0, ea1, eb0, eb1;
     h4 sa0, sa1, sb0, sb1;
   };
-  uint32_t hmask = h ? 0u : 0xFFFFu;     // k 0 of the outer product lives in lanes 0-31
-  asm volatile("" : "+v"(hmask));
   auto load_ops = [&](auto buf_c, auto g_c) {
     constexpr int buf = decltype(buf_c)::value;
     constexpr int g = decltype(g_c)::value;
@@ -1136,11 +1136,14 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
     o.ea1 = lds_s[buf][0][g][wn * 64 + 32 + l32];
     o.eb0 = lds_s[buf][1][g][wm * 64 + l32];
     o.eb1 = lds_s[buf][1][g][wm * 64 + 32 + l32];
-    auto op = [&](uint32_t v) { return __builtin_bit_cast(h4, make_uint2(v & hmask, 0u)); };
-    o.sa0 = op(o.ea0);
-    o.sa1 = op(o.ea1);
-    o.sb0 = op(o.eb0);
-    o.sb1 = op(o.eb1);
+    // outer-product operands: k 0 (lanes 0-31) and k 4 (lanes 32-63) both
+    // carry the significand, so the product comes out doubled (exactly;
+    // the X exponent byte is one lower to cancel it); the W word's exponent
+    // byte lands in k 1 / k 5, where the X operand is zero
+    o.sa0 = __builtin_bit_cast(h4, make_uint2(o.ea0, 0u));
+    o.sa1 = __builtin_bit_cast(h4, make_uint2(o.ea1, 0u));
+    o.sb0 = __builtin_bit_cast(h4, make_uint2(o.eb0 & 0xFFFFu, 0u));
+    o.sb1 = __builtin_bit_cast(h4, make_uint2(o.eb1 & 0xFFFFu, 0u));
     return o;
   };
   // tile-group t = 2 it + jt: the group's partial P of W tile it and X
@@ -1153,9 +1156,10 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   };
   // Scale outer product of tile-group t.  The products m_w(n) m_x(m) of
   // the scale significands form a rank-1 32 x 32 matrix:
-  // v_mfma_f32_32x32x8_f16 with k 0 holding m_w (A, lanes 0-31) and m_x (B)
-  // and k 1..7 zero returns it exactly in fp32, in the accumulator layout of
-  // P, so that the dequant (dqc) is one fp32 FMA per element on the VALU.
+  // v_mfma_f32_32x32x8_f16 with k 0 and k 4 holding m_w (A) and m_x (B)
+  // returns it, doubled, exactly in fp32 and in the accumulator layout of P
+  // (the doubling is cancelled by the X exponent), so that the dequant
+  // (dqc) is one fp32 FMA per element on the VALU.
   const v16f zero16 = {};
   auto rk = [&](const Ops& o, auto t_c) {
     constexpr int t = decltype(t_c)::value;
