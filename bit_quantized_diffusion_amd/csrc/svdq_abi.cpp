@@ -137,6 +137,7 @@ int svdq_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs, const uint8_t* wq,
   if (M < 1 || N < 1) return SVDQ_ERR_SHAPE;
   if ((st = check_k(K, precision))) return st;
   if ((st = check_rank(rank, K, N))) return st;
+  if ((st = check_operand_extent(M, K, precision)) || (st = check_operand_extent(N, K, precision))) return st;
   if ((st = current_device_ok())) return st;
   return hip_status(svdq_launch_gemm_w4a4_lora_up(xq, xs, wq, ws, lora_act, lora_up, bias, y, M, N, K, rank,
                                                   precision, stream));
@@ -157,6 +158,7 @@ int svdq_gemm_w4a4_lora_up_gelu(const uint8_t* xq, const void* xs, const uint8_t
   if (M < 1 || N < 1) return SVDQ_ERR_SHAPE;
   if ((st = check_k(K, precision))) return st;
   if ((st = check_rank(rank, K, N))) return st;
+  if ((st = check_operand_extent(M, K, precision)) || (st = check_operand_extent(N, K, precision))) return st;
   if ((st = current_device_ok())) return st;
   return hip_status(svdq_launch_gemm_int4_gelu(xq, xs, wq, ws, lora_act, lora_up, bias, y, M, N, K, rank, stream));
 }
@@ -181,6 +183,9 @@ int svdq_mlp_gemm_gelu_quant(const uint8_t* xq, const void* xs, const uint8_t* w
   if ((st = check_k(K, precision))) return st;
   if ((st = check_rank(rank, K, N))) return st;
   if ((st = check_rank(rank2, N, N))) return st;
+  if ((st = check_operand_extent(M, K, precision)) || (st = check_operand_extent(N, K, precision)) ||
+      (st = check_operand_extent(M, N, precision)))
+    return st;
   if ((st = current_device_ok())) return st;
   return hip_status(svdq_launch_mlp_gemm_gelu_quant(xq, xs, wq, ws, lora_act, lora_up, bias, M, N, K, rank,
                                                     smooth_inv2, lora_down2, rank2, xq2, xs2, lora_act2, stream));
@@ -194,6 +199,7 @@ int svdq_gemm_w4a16(const void* x, const uint8_t* wq, const void* ws, const void
   if (M < 1 || N < 1) return SVDQ_ERR_SHAPE;
   int st;
   if ((st = check_k(K, SVDQ_INT4))) return st;
+  if ((st = check_operand_extent(N, K, SVDQ_INT4))) return st;
   if ((st = current_device_ok())) return st;
   return hip_status(svdq_launch_gemm_w4a16(x, wq, ws, bias, y, M, N, K, stream));
 }
@@ -214,6 +220,7 @@ int svdq_unfused_linear(const void* x, int M, int K, const float* smooth_inv, co
   if ((st = check_k(K, precision))) return st;
   if ((st = check_rank(rank, K, N))) return st;
   if (precision != SVDQ_INT4) return SVDQ_ERR_INVALID_ARG;
+  if ((st = check_operand_extent(M, K, precision)) || (st = check_operand_extent(N, K, precision))) return st;
   if ((st = current_device_ok())) return st;
   return hip_status(svdq_launch_unfused_linear(x, M, K, smooth_inv, lora_down, rank, wq, ws, lora_up, bias, N,
                                                precision, xq, xs, lora_act, y, stream));
@@ -237,6 +244,7 @@ int svdq_debug_group_partials(const uint8_t* xq, const uint8_t* wq, int M, int N
   if (st) return st;
   if (m0 < 0 || n0 < 0 || m0 + static_cast<long long>(mt) > M || n0 + static_cast<long long>(nt) > N)
     return SVDQ_ERR_SHAPE;
+  if ((st = check_operand_extent(M, K, SVDQ_INT4)) || (st = check_operand_extent(N, K, SVDQ_INT4))) return st;
   if ((st = current_device_ok())) return st;
   return hip_status(svdq_launch_debug_group_partials(xq, wq, M, N, K, m0, n0, mt, nt, out, stream));
 }

@@ -20,6 +20,7 @@ int host_threads();
 int check_precision(int precision);
 int check_k(int K, int precision);
 int check_rank(int rank, int K, int N);
+int check_operand_extent(int rows, int K, int precision);
 
 // Host-side number-format helpers used by the offline pack.
 uint16_t f32_to_bf16_bits(float f);

@@ -1419,15 +1419,18 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_w4a16(
 
 // K1 grid: 64-row blocks x K slices.  The slice count is chosen so that
 // the grid holds about four workgroups per CU (256 CUs), with slices of
-// whole 128-k steps.
+// whole 128-k steps and at most kK1MaxSliceSteps steps, which bounds the
+// slice's smooth_inv staging in LDS at 8 KB for any M and K.
 template <int RT, int QMODE = kQuantInt4>
 hipError_t launch_k1(const void* x, int M, int K, const float* sinv, const void* ldown, uint8_t* xq, void* xs,
                      float* lact, hipStream_t st) {
   const int row_blocks = (M + kK1Rows - 1) / kK1Rows;
   const int steps = (K + 127) / 128;
+  constexpr int kK1MaxSliceSteps = 16;
   int slices = (1024 + row_blocks - 1) / row_blocks;
   if (slices > steps) slices = steps;
   if (slices < 1) slices = 1;
+  if (slices < (steps + kK1MaxSliceSteps - 1) / kK1MaxSliceSteps) slices = (steps + kK1MaxSliceSteps - 1) / kK1MaxSliceSteps;
   const int steps_per_slice = (steps + slices - 1) / slices;
   const int ks = steps_per_slice * 128;
   slices = (steps + steps_per_slice - 1) / steps_per_slice;
@@ -1701,3 +1704,4 @@ extern "C" int svdq_launch_debug_group_partials(const uint8_t* xq, const uint8_t
                      nullptr, wq, nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, 0, m0, n0, mt, nt, out, MlpOut{});
   return static_cast<int>(hipGetLastError());
 }
+

@@ -109,6 +109,16 @@ int check_k(int K, int precision) {
   return SVDQ_OK;
 }
 
+// The GEMM kernels address a 4-bit operand and its scale array with 32-bit
+// byte offsets: rows * K/2 code bytes and (K / group) * rows scale bytes
+// must stay below 2^31 (M or N up to ~349,000 at K = 12288).
+int check_operand_extent(int rows, int K, int precision) {
+  const long long codes = static_cast<long long>(rows) * (K / 2);
+  const long long scales = precision == SVDQ_INT4 ? static_cast<long long>(K / kInt4Group) * rows * 2
+                                                  : static_cast<long long>(K / kMxBlock) * rows;
+  return (codes < (1LL << 31) && scales < (1LL << 31)) ? SVDQ_OK : SVDQ_ERR_SHAPE;
+}
+
 int check_rank(int rank, int K, int N) {
   if (rank < 0 || rank % 16 != 0 || rank > kMaxRank) return SVDQ_ERR_SHAPE;
   if (rank > std::min(K, N)) return SVDQ_ERR_SHAPE;

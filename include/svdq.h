@@ -45,7 +45,11 @@
  *    MXFP4 scales: E8M0 bytes, one per 32 k, group-major [K/32][rows].
  *  - Shapes: M, N >= 1 (any value); K >= 64 and K % 64 == 0 for INT4,
  *    K % 128 == 0 for MXFP4; rank == 0 (no low-rank branch) or a multiple of
- *    16, at most 256 and at most min(K, N).
+ *    16, at most 256 and at most min(K, N).  The GEMM calls address each
+ *    4-bit operand and its scale array with 32-bit byte offsets: rows * K/2
+ *    code bytes and the scale bytes of X (rows = M) and of W (rows = N)
+ *    must each stay below 2^31, else SVDQ_ERR_SHAPE (M or N up to ~349,000
+ *    at K = 12288).
  *  - Device pointers must be 16-byte aligned.
  *  - Errors: arguments and the device are checked before anything is
  *    launched and reported as a status code; nothing is thrown across the
@@ -276,8 +280,12 @@ SVDQ_API int svdq_unfused_linear(const void* x, int M, int K,
 SVDQ_API int svdq_bench_mfma_ceiling(int precision, int blocks, int iters, float* out, void* stream);
 
 /* Test hook: the exact per-group integer partials of the INT4 GEMM for the
- * output window rows [m0, m0+mt) x columns [n0, n0+nt), computed by the
- * same device code as svdq_gemm_w4a4_lora_up.
+ * output window rows [m0, m0+mt) x columns [n0, n0+nt).  It runs the INT4
+ * GEMM kernel of svdq_gemm_w4a4_lora_up in a test mode that shares its code
+ * loader, the conversion of the codes for the matrix core, the LDS layout
+ * and the matrix instruction that forms each group's partial; the scale
+ * handling (the per-group dequant into the accumulators), the up
+ * projection and the epilogue are replaced by a store of the partials.
  *   out (dev) [mt][nt][K/64] int32.  mt, nt >= 1; the window must lie
  *   inside [0, M) x [0, N). */
 SVDQ_API int svdq_debug_group_partials(const uint8_t* xq, const uint8_t* wq,

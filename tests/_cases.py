@@ -86,3 +86,69 @@ def mx_oracle_rows(case, rows, x_bits=None):
     b = O.mx_gemm_lora_up(a["xq"], a["xs"], pk["wq"], pk["ws"], a["t"], pk["l2"], case["bias"])
     b.update(a)
     return b
+
+
+# ---------------------------------------------------------------------------
+# per-element output bounds (from the oracle's own terms, never from the GPU)
+# ---------------------------------------------------------------------------
+
+def ulp_bf16(v) -> np.ndarray:
+    """Spacing of bf16 values at |v| (bf16 keeps 8 significant bits; below
+    2^-126 the spacing is that of the subnormals, 2^-133)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(np.where(a > 0, e, -126), -126)
+    return np.exp2(e - 7)
+
+
+def int4_slack(ref, xs, ws, t, l2_bits, bias_bits, t_from_kernel):
+    """Per-element slack of the fp32 pre-rounding sum against the oracle's
+    exact one, for an INT4 layer whose oracle terms are in `ref`
+    (gemm_w4a4_lora_up's P).
+
+    The GPU adds the G dequantized group partials with one fp32 FMA each,
+    the rank-r up projection with fp32 matrix-core accumulation and the
+    bias, so its sum differs from the exact one by at most about
+    (G + r + 2) fp32 roundings of the running magnitude; twice that is used.
+    When lora_act comes from the GPU's kernel 1 (a different summation order
+    than the oracle's fp64), bf16(t) can land one bf16 step away: one
+    ulp_bf16(t_j) |L2_jn| per rank component is allowed for it."""
+    P = np.abs(np.asarray(ref["P"], dtype=np.float64))          # [M][N][G]
+    sx = np.asarray(xs).astype(np.float64)                      # [G][M]
+    sw = np.asarray(ws).astype(np.float64)                      # [G][N]
+    A = np.einsum("mng,gm,gn->mn", P, sx, sw)
+    G = P.shape[2]
+    l2 = O.bf16_bits_to_f32(l2_bits).astype(np.float64)
+    r = l2.shape[0]
+    U = np.zeros_like(A)
+    T = np.zeros_like(A)
+    if r:
+        tb = O.bf16_bits_to_f32(O.f32_to_bf16_bits(np.asarray(t).astype(np.float32))).astype(np.float64)
+        U = np.abs(tb) @ np.abs(l2)
+        if t_from_kernel:
+            T = ulp_bf16(np.asarray(t, np.float64)) @ np.abs(l2)
+    B = np.zeros(A.shape[1]) if bias_bits is None else np.abs(O.bf16_bits_to_f32(bias_bits).astype(np.float64))
+    gamma = 2.0 * (G + r + 2) * 2.0 ** -24
+    return gamma * (A + U + B[None, :]) + T
+
+
+def mx_slack(ref_a_xq, ref_a_xs, wq, ws, t, l2_bits, bias_bits, t_from_kernel):
+    """As int4_slack for the MXFP4 layer: the decoded operands' |a||b| sum
+    replaces the per-group partials; the matrix core accumulates K/64
+    instructions' results in fp32."""
+    a = np.abs(O.mx_decode(O.mxfp4_oracle._unpack_nibbles(ref_a_xq), np.asarray(ref_a_xs).T))
+    b = np.abs(O.mx_decode(O.mxfp4_oracle._unpack_nibbles(wq), np.asarray(ws).T))
+    A = a @ b.T
+    K = a.shape[1]
+    l2 = O.bf16_bits_to_f32(l2_bits).astype(np.float64)
+    r = l2.shape[0]
+    U = np.zeros_like(A)
+    T = np.zeros_like(A)
+    if r:
+        tb = O.bf16_bits_to_f32(O.f32_to_bf16_bits(np.asarray(t).astype(np.float32))).astype(np.float64)
+        U = np.abs(tb) @ np.abs(l2)
+        if t_from_kernel:
+            T = ulp_bf16(np.asarray(t, np.float64)) @ np.abs(l2)
+    B = np.zeros(A.shape[1]) if bias_bits is None else np.abs(O.bf16_bits_to_f32(bias_bits).astype(np.float64))
+    gamma = 2.0 * (K // 64 + r + 2) * 2.0 ** -24
+    return gamma * (A + U + B[None, :]) + T

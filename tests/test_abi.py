@@ -104,6 +104,32 @@ def test_hot_calls_reject_bad_shapes():
     assert L.svdq_debug_group_partials(FAKE, FAKE, 16, 16, 64, 10, 0, 7, 1, FAKE, None) == bq.SVDQ_ERR_SHAPE
 
 
+def test_oversize_operands_are_refused():
+    """The GEMMs address a 4-bit operand and its scales with 32-bit byte
+    offsets, so an operand of 2^31 code bytes or more is refused with
+    SVDQ_ERR_SHAPE before anything is launched (never a wrong Y): M = N =
+    349,526 at K = 12288 is the first such size; one token fewer passes the
+    shape rules (and then stops at the device check here)."""
+    L = bq.lib
+    K = 12288
+    big, ok = 349526, 349525
+    assert big * (K // 2) >= 2 ** 31 > ok * (K // 2)
+    for prec in (bq.INT4, bq.MXFP4):
+        g = L.svdq_gemm_w4a4_lora_up
+        assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, big, 64, K, 16, prec, None) == bq.SVDQ_ERR_SHAPE
+        assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, big, K, 16, prec, None) == bq.SVDQ_ERR_SHAPE
+        assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ok, 64, K, 16, prec, None) != bq.SVDQ_ERR_SHAPE
+    assert L.svdq_gemm_w4a4_lora_up_gelu(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, big, 64, K, 16, 0, None) \
+        == bq.SVDQ_ERR_SHAPE
+    assert L.svdq_unfused_linear(FAKE, big, K, FAKE, FAKE, 16, FAKE, FAKE, FAKE, None, 64, 0, FAKE, FAKE, FAKE, FAKE,
+                                 None) == bq.SVDQ_ERR_SHAPE
+    assert L.svdq_gemm_w4a16(FAKE, FAKE, FAKE, None, FAKE, 64, big, K, None) == bq.SVDQ_ERR_SHAPE
+    assert L.svdq_debug_group_partials(FAKE, FAKE, big, 16, K, 0, 0, 1, 1, FAKE, None) == bq.SVDQ_ERR_SHAPE
+    f = L.svdq_mlp_gemm_gelu_quant
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, big, 256, K, 16, FAKE, FAKE, 16, 0, FAKE, FAKE, FAKE,
+             None) == bq.SVDQ_ERR_SHAPE
+
+
 def test_mlp_calls_validate():
     """The GELU and fused-MLP calls: NULL / misaligned pointers, MXFP4
     (INT4 only), N not a multiple of 128 for the fused pair, rank rules."""

@@ -114,7 +114,8 @@ def test_mx_k2_parity(p):
     y = bq.gemm_w4a4_lora_up(dev(ref["xq"]), dev(ref["xs"]), layer.wq, layer.ws, la, layer.lora_up,
                              layer.bias, M, N, K, r, bq.MXFP4)
     torch.cuda.synchronize()
-    assert_y_close(host_u16(y), ref["y"], "mx k2")
+    sl = C.mx_slack(ref["xq"], ref["xs"], pk["wq"], pk["ws"], ref["t"], pk["l2"], case["bias"], t_from_kernel=False)
+    assert_y_close(host_u16(y), ref["y"], "mx k2", sl, ref["y64"])
 
 
 @pytest.mark.parametrize("spread", [(120, 134), (100, 150), (0, 0)], ids=["near1", "wide", "zero"])
@@ -140,7 +141,8 @@ def test_mx_k2_block_scales(spread):
     if hi == 0:
         assert np.all(O.bf16_bits_to_f32(yb) == 0)
         return
-    assert_y_close(yb, ref["y"], "mx block scales")
+    sl = C.mx_slack(xq, sx, wq, sw, np.zeros((M, 0)), np.zeros((0, N), np.uint16), None, t_from_kernel=False)
+    assert_y_close(yb, ref["y"], "mx block scales", sl, ref["y64"])
     got = O.bf16_bits_to_f32(yb).astype(np.float64)
     want = ref["y64"]
     row_err = np.max(np.abs(got - want), axis=1)
@@ -156,7 +158,8 @@ def test_mx_layer_end_to_end(p):
     ref = C.mx_oracle_rows(case, np.arange(M))
     y = bq.linear(dev_bf16(case["x"]), _mx_layer(case, pk))
     torch.cuda.synchronize()
-    assert_y_close(host_u16(y), ref["y"], "mx layer")
+    sl = C.mx_slack(ref["xq"], ref["xs"], pk["wq"], pk["ws"], ref["t"], pk["l2"], case["bias"], t_from_kernel=True)
+    assert_y_close(host_u16(y), ref["y"], "mx layer", sl, ref["y64"])
 
 
 def test_mx_full_size_fc1():
@@ -181,4 +184,5 @@ def test_mx_full_size_fc1():
     rng = np.random.default_rng(5)
     rows = np.unique(np.concatenate([[0, 1, 127, 128, M - 1], rng.choice(M, 27, replace=False)]))
     ref = C.mx_oracle_rows(case, rows)
-    assert_y_close(host_u16(y)[rows], ref["y"], "mx fc1 end to end")
+    sl = C.mx_slack(ref["xq"], ref["xs"], pk["wq"], pk["ws"], ref["t"], pk["l2"], case["bias"], t_from_kernel=True)
+    assert_y_close(host_u16(y)[rows], ref["y"], "mx fc1 end to end", sl, ref["y64"])

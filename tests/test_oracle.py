@@ -465,3 +465,157 @@ def test_gelu_tanh_form():
     t = O.gelu_tanh(np.array([-10.0, -1e4]))
     assert t[0] < 0 and t[0] > -1e-30          # tiny, not rounded to 0 by cancellation
     assert t[1] == 0.0 and np.signbit(t[1])    # exp overflow: -0
+
+
+# ---------------------------------------------------------------------------
+# smoothing of the activations: one rounding to fp32, then one to bf16 (R7)
+# ---------------------------------------------------------------------------
+
+def _bf16r(x: Fraction) -> Fraction:
+    return round_to_format(x, 8, -126)
+
+
+def _double_rounding_pairs(n_want=24, seed=31):
+    """(x, s) pairs, x bf16 and s fp32, whose exact product rounds to a
+    different bf16 value directly than through fp32: the fp32 rounding lands
+    on a bf16 halfway point.  Found by a seeded search over products that
+    are exact in fp64 (8 x 24 significant bits)."""
+    rng = np.random.default_rng(seed)
+    found = []
+    while len(found) < n_want:
+        x = O.bf16_bits_to_f32(rng.integers(0x3C00, 0x4300, 1 << 16).astype(np.uint16))
+        s = (1.0 + rng.random(1 << 16)).astype(np.float32)
+        p = x.astype(np.float64) * s.astype(np.float64)      # exact
+        p32 = p.astype(np.float32).view(np.uint32)
+        tie = (p32 & 0xFFFF) == 0x8000                        # fp32 value is a bf16 halfway point
+        for i in np.nonzero(tie)[0]:
+            exact = Fraction(float(x[i])) * Fraction(float(s[i]))
+            if _bf16r(exact) != _bf16r(f32r(exact)):
+                found.append((np.float32(x[i]), np.float32(s[i])))
+    return found[:n_want]
+
+
+def test_smooth_act_rounds_through_fp32_then_bf16():
+    """x^ = bf16(fp32(x * smooth_inv)): checked in exact rationals on products
+    where rounding straight from the exact (or fp64) product, or skipping
+    the bf16 step, gives a different value."""
+    pairs = _double_rounding_pairs()
+    x = np.array([p[0] for p in pairs], np.float32)
+    s = np.array([p[1] for p in pairs], np.float32)
+    # one row per pair, smooth_inv per column: put pair i on the diagonal
+    n = len(pairs)
+    xb = np.zeros((n, n), np.uint16)
+    xb[np.arange(n), np.arange(n)] = O.f32_to_bf16_bits(x)
+    got = O.smooth_act(xb, s)
+    for i in range(n):
+        exact = Fraction(float(x[i])) * Fraction(float(s[i]))
+        want = _bf16r(f32r(exact))
+        assert Fraction(float(O.bf16_bits_to_f32(got[i:i + 1, i])[0])) == want
+        assert want != _bf16r(exact)          # the single rounding would differ
+        assert want != f32r(exact)            # and the unrounded fp32 value too
+    # off-diagonal zeros stay zero
+    off = got.copy()
+    off[np.arange(n), np.arange(n)] = 0
+    assert not off.any()
+
+
+def test_smooth_act_random_against_rationals():
+    rng = np.random.default_rng(32)
+    xb = rng.integers(0, 0x7F00, (6, 40)).astype(np.uint16) | (rng.integers(0, 2, (6, 40)) << 15).astype(np.uint16)
+    s = (rng.standard_normal(40) * np.exp2(rng.integers(-8, 8, 40))).astype(np.float32)
+    got = O.smooth_act(xb, s)
+    xf = O.bf16_bits_to_f32(xb)
+    for m in range(6):
+        for k in range(40):
+            want = _bf16r(f32r(Fraction(float(xf[m, k])) * Fraction(float(s[k]))))
+            assert Fraction(float(O.bf16_bits_to_f32(got[m:m + 1, k])[0])) == want
+
+
+# ---------------------------------------------------------------------------
+# MXFP4: several blocks of one row with their own scales
+# ---------------------------------------------------------------------------
+
+def test_mx_decode_multi_block_row():
+    """A row of 4 blocks with scale bytes 127, 120, 133, 0: each element is
+    sign * grid[code & 7] * 2^(byte - 127) of its own block (hand sum)."""
+    grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    rng = np.random.default_rng(41)
+    codes = rng.integers(0, 16, (2, 128)).astype(np.uint8)
+    sb = np.array([[127, 120, 133, 0], [1, 254, 126, 128]], np.uint8)
+    dec = O.mx_decode(codes, sb)
+    for r in range(2):
+        for k in range(128):
+            c = int(codes[r, k])
+            want = (-1.0 if c & 8 else 1.0) * grid[c & 7] * 2.0 ** (int(sb[r, k // 32]) - 127)
+            assert dec[r, k] == want, (r, k)
+
+
+def test_mx_gemm_multi_block_hand_sum():
+    """mx_gemm_lora_up on rows with distinct per-block scales against an
+    explicit double loop over k with each element decoded by hand."""
+    grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    rng = np.random.default_rng(42)
+    M, N, K = 3, 4, 128
+    cx = rng.integers(0, 16, (M, K)).astype(np.uint8)
+    cw = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    bx = rng.integers(110, 140, (M, K // 32)).astype(np.uint8)
+    bw = rng.integers(110, 140, (N, K // 32)).astype(np.uint8)
+    pack = lambda c: (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+    out = O.mx_gemm_lora_up(pack(cx), np.ascontiguousarray(bx.T), pack(cw), np.ascontiguousarray(bw.T),
+                            np.zeros((M, 0)), np.zeros((0, N), np.uint16), None)
+
+    def dec(c, b):
+        return (-1.0 if c & 8 else 1.0) * grid[c & 7] * 2.0 ** (int(b) - 127)
+
+    for m in range(M):
+        for n in range(N):
+            s = Fraction(0)
+            for k in range(K):
+                s += Fraction(dec(int(cx[m, k]), bx[m, k // 32])) * Fraction(dec(int(cw[n, k]), bw[n, k // 32]))
+            assert out["y64"][m, n] == float(s)      # exact: dyadic values well inside fp64
+            assert out["y"][m, n] == O.f32_to_bf16_bits(np.array([float(s)], np.float32))[0]
+
+
+# ---------------------------------------------------------------------------
+# R8 (the up projection reads bf16(t)) and R9 (one rounding of acc + up + b)
+# ---------------------------------------------------------------------------
+
+def _one_code_group(q_x, q_w, s_x, s_w):
+    """One token, one channel, K = 64: a single non-zero code pair at k 0."""
+    qx = np.zeros((1, 64), np.int8)
+    qw = np.zeros((1, 64), np.int8)
+    qx[0, 0], qw[0, 0] = q_x, q_w
+    xs = np.array([[s_x]], np.float16)
+    ws = np.array([[s_w]], np.float16)
+    return O.pack_int4(qx), xs, O.pack_int4(qw), ws
+
+
+def test_up_projection_uses_bf16_of_t():
+    """acc = 1 * 1 * 2^-4 * 2^-4 = 2^-8; t = 1 + 2^-10 is not a bf16 value
+    and rounds to 1; L2 = 1.  With bf16(t): y = 1 + 2^-8, a bf16 halfway
+    point, which rounds to the even 1.0 (0x3F80).  With t unrounded the sum
+    is above the halfway point and would give 1 + 2^-7 (0x3F81)."""
+    xq, xs, wq, ws = _one_code_group(1, 1, 2.0 ** -4, 2.0 ** -4)
+    t = np.array([[1.0 + 2.0 ** -10]])
+    l2 = O.f32_to_bf16_bits(np.array([[1.0]], np.float32))
+    out = O.gemm_w4a4_lora_up(xq, xs, wq, ws, t, l2, None)
+    assert out["acc"][0, 0] == 2.0 ** -8
+    assert out["up"][0, 0] == 1.0
+    assert int(out["y"][0, 0]) == 0x3F80
+
+
+def test_output_rounded_once_after_bias():
+    """acc = 2^-8 (one code pair, scales 2^-4), up = 1 (t = 1, L2 = 1),
+    bias = 2^-12: the exact sum 1 + 2^-8 + 2^-12 lies above the bf16
+    halfway point 1 + 2^-8 and rounds up to 1 + 2^-7 (0x3F81).  Rounding
+    acc + up first (to the even 1.0) and then adding the bias would give
+    0x3F80."""
+    xq, xs, wq, ws = _one_code_group(1, 1, 2.0 ** -4, 2.0 ** -4)
+    t = np.array([[1.0]])
+    l2 = O.f32_to_bf16_bits(np.array([[1.0]], np.float32))
+    bias = O.f32_to_bf16_bits(np.array([2.0 ** -12], np.float32))
+    out = O.gemm_w4a4_lora_up(xq, xs, wq, ws, t, l2, bias)
+    assert out["y64"][0, 0] == 1.0 + 2.0 ** -8 + 2.0 ** -12
+    assert int(out["y"][0, 0]) == 0x3F81
+    # the per-group partial times both scales, by hand: 1 * 2^-4 * 2^-4
+    assert out["P"][0, 0, 0] == 1 and out["acc"][0, 0] == 2.0 ** -8
