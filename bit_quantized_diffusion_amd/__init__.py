@@ -28,6 +28,7 @@ __all__ = [
     "INT4", "MXFP4", "SvdqError", "lib", "LIB_PATH", "status_string", "merge_lora",
     "version", "device_check", "packed_sizes", "act_sizes", "pack_weights",
     "quantize_act_lora_down", "gemm_w4a4_lora_up", "debug_group_partials", "unfused_linear",
+    "unfused_linear_noalloc", "NOALLOC_SCRATCH_BYTES",
     "PackedLinear", "linear", "gemm_w4a4_lora_up_gelu", "mlp_gemm_gelu_quant", "mlp",
     "pack_w4a16", "gemm_w4a16", "mfma_ceiling",
 ]
@@ -303,6 +304,27 @@ def unfused_linear(x, layer: "PackedLinear", y=None, xq=None, xs=None, lora_act=
         _dptr(layer.bias, torch.bfloat16, (N,), "bias"), N, layer.precision,
         _dptr(xq, torch.uint8, (M, K // 2), "xq"), _dptr(xs, torch.float16, (K // 64, M), "xs"),
         _dptr(lora_act, torch.float32, (M, r), "lora_act") if r else None,
+        _dptr(y, torch.bfloat16, (M, N), "y"), _stream(dev)))
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def unfused_linear_noalloc(x, layer: "PackedLinear", y):
+    """unfused_linear with its intermediates in the library's own device
+    array (svdq_unfused_linear_noalloc): the caller passes y and nothing is
+    allocated.  Calls that overlap on one GPU race."""
+    torch = _torch()
+    M, K = x.shape
+    N, r, dev = layer.N, layer.rank, x.device
+    check(lib.svdq_unfused_linear_noalloc(
+        _dptr(x, torch.bfloat16, (M, K), "x"), M, K,
+        _dptr(layer.smooth_inv, torch.float32, (K,), "smooth_inv"),
+        _dptr(layer.lora_down, torch.bfloat16, (r, K), "lora_down") if r else None, r,
+        _dptr(layer.wq, torch.uint8, (N, K // 2), "wq"), _dptr(layer.ws, torch.float16, (K // 64, N), "ws"),
+        _dptr(layer.lora_up, torch.bfloat16, (N, r), "lora_up") if r else None,
+        _dptr(layer.bias, torch.bfloat16, (N,), "bias"), N, layer.precision,
         _dptr(y, torch.bfloat16, (M, N), "y"), _stream(dev)))
     return y
 

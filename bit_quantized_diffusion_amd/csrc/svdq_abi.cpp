@@ -16,6 +16,8 @@
 
 using namespace svdq;
 
+static_assert(kNoAllocScratchBytes == SVDQ_NOALLOC_SCRATCH_BYTES, "scratch size of the header and the library agree");
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -224,6 +226,29 @@ int svdq_unfused_linear(const void* x, int M, int K, const float* smooth_inv, co
   if ((st = current_device_ok())) return st;
   return hip_status(svdq_launch_unfused_linear(x, M, K, smooth_inv, lora_down, rank, wq, ws, lora_up, bias, N,
                                                precision, xq, xs, lora_act, y, stream));
+}
+
+int svdq_unfused_linear_noalloc(const void* x, int M, int K, const float* smooth_inv, const void* lora_down,
+                                int rank, const uint8_t* wq, const void* ws, const void* lora_up, const void* bias,
+                                int N, int precision, void* y, void* stream) {
+  int st = check_precision(precision);
+  if (st) return st;
+  if (!x || !smooth_inv || !wq || !ws || !y) return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!lora_down || !lora_up)) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(smooth_inv) || !aligned16(wq) || !aligned16(ws) || !aligned16(y))
+    return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!aligned16(lora_down) || !aligned16(lora_up))) return SVDQ_ERR_INVALID_ARG;
+  if (bias && !aligned16(bias)) return SVDQ_ERR_INVALID_ARG;
+  if (M < 1 || N < 1) return SVDQ_ERR_SHAPE;
+  if ((st = check_k(K, precision))) return st;
+  if ((st = check_rank(rank, K, N))) return st;
+  if (precision != SVDQ_INT4) return SVDQ_ERR_INVALID_ARG;
+  if ((st = check_operand_extent(M, K, precision)) || (st = check_operand_extent(N, K, precision))) return st;
+  size_t off[3];
+  if (noalloc_layout(M, K, rank, off) > kNoAllocScratchBytes) return SVDQ_ERR_SHAPE;
+  if ((st = current_device_ok())) return st;
+  return hip_status(svdq_launch_unfused_linear_noalloc(x, M, K, smooth_inv, lora_down, rank, wq, ws, lora_up, bias, N,
+                                                       precision, y, stream));
 }
 
 int svdq_bench_mfma_ceiling(int precision, int blocks, int iters, float* out, void* stream) {

@@ -22,6 +22,19 @@ int check_k(int K, int precision);
 int check_rank(int rank, int K, int N);
 int check_operand_extent(int rows, int K, int precision);
 
+// Device scratch of svdq_unfused_linear_noalloc: its codes, scales and
+// lora_act, each at a 256-byte aligned offset.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+inline size_t noalloc_align(size_t v) { return (v + 255) & ~size_t(255); }
+// off[0] xq, off[1] xs, off[2] lora_act; returns the bytes the call needs.
+inline size_t noalloc_layout(int M, int K, int rank, size_t off[3]) {
+  const size_t m = static_cast<size_t>(M), k = static_cast<size_t>(K), r = static_cast<size_t>(rank);
+  off[0] = 0;
+  off[1] = noalloc_align(m * k / 2);
+  off[2] = off[1] + noalloc_align((k / kInt4Group) * m * 2);
+  return off[2] + m * r * 4;
+}
+
 // Host-side number-format helpers used by the offline pack.
 uint16_t f32_to_bf16_bits(float f);
 float bf16_bits_to_f32(uint16_t b);
@@ -60,6 +73,9 @@ int svdq_launch_unfused_linear(const void* x, int M, int K,
                                int precision, uint8_t* xq, void* xs,
                                float* lora_act, void* y, void* stream);
 int svdq_launch_mfma_ceiling(int precision, int blocks, int iters, float* out, void* stream);
+int svdq_launch_unfused_linear_noalloc(const void* x, int M, int K, const float* smooth_inv, const void* lora_down,
+                                       int rank, const uint8_t* wq, const void* ws, const void* lora_up,
+                                       const void* bias, int N, int precision, void* y, void* stream);
 int svdq_launch_debug_group_partials(const uint8_t* xq, const uint8_t* wq,
                                      int M, int N, int K, int m0, int n0,
                                      int mt, int nt, int32_t* out,

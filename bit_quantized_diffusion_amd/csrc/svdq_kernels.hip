@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "svdq_internal.h"
 
 namespace {
@@ -1705,3 +1707,52 @@ extern "C" int svdq_launch_debug_group_partials(const uint8_t* xq, const uint8_t
   return static_cast<int>(hipGetLastError());
 }
 
+// ---------------------------------------------------------------------------
+// The unfused layer without workspace arguments, for callers that cannot
+// allocate: its intermediates (codes, scales, lora_act) live in one
+// file-scope device array of kNoAllocScratchBytes, the same array for every
+// call on a device.  Host code never uses the array's name as an address:
+// the device address comes from hipGetSymbolAddress, taken once per device
+// (with that device current) on the first call there, and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[svdq::kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+void* g_scratch_ptr[kScratchDevices];
+std::mutex g_scratch_mutex;
+
+hipError_t scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" int svdq_launch_unfused_linear_noalloc(const void* x, int M, int K, const float* smooth_inv,
+                                                  const void* lora_down, int rank, const uint8_t* wq, const void* ws,
+                                                  const void* lora_up, const void* bias, int N, int precision, void* y,
+                                                  void* stream) {
+  void* base = nullptr;
+  const hipError_t e = scratch_ptr(&base);
+  if (e != hipSuccess) return static_cast<int>(e);
+  size_t off[3];
+  svdq::noalloc_layout(M, K, rank, off);
+  uint8_t* b = static_cast<uint8_t*>(base);
+  return svdq_launch_unfused_linear(x, M, K, smooth_inv, lora_down, rank, wq, ws, lora_up, bias, N, precision,
+                                    b + off[0], b + off[1], rank > 0 ? reinterpret_cast<float*>(b + off[2]) : nullptr,
+                                    y, stream);
+}

@@ -270,6 +270,26 @@ SVDQ_API int svdq_unfused_linear(const void* x, int M, int K,
                         uint8_t* xq, void* xs, float* lora_act, void* y,
                         void* stream);
 
+/* svdq_unfused_linear for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same four kernels and the same result, without the xq, xs and lora_act
+ * workspace arguments.  Those intermediates live in one device array of
+ * 32 MiB (SVDQ_NOALLOC_SCRATCH_BYTES) that the library holds on every GPU
+ * it runs on until the process ends; the call itself allocates nothing.
+ * The array needs M*K/2 + (K/64)*M*2 + M*rank*4 bytes, each part rounded up
+ * to 256 bytes (FLUX.1's 12288 -> 3072 MLP layer at M = 4608, rank 32:
+ * ~30.7 MB); a larger call returns SVDQ_ERR_SHAPE.  Every call on a GPU
+ * shares that GPU's array and leaves its contents behind, so calls that
+ * overlap on one GPU (two streams, two threads) race and must be
+ * serialized by the caller.  INT4 only; other arguments and errors as for
+ * svdq_unfused_linear. */
+#define SVDQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+SVDQ_API int svdq_unfused_linear_noalloc(const void* x, int M, int K,
+                        const float* smooth_inv, const void* lora_down, int rank,
+                        const uint8_t* wq, const void* ws,
+                        const void* lora_up, const void* bias, int N, int precision,
+                        void* y, void* stream);
+
 /* Measurement hook: the dense matrix-core rate this GPU sustains.  Each of
  * `blocks` workgroups (4 waves; launch two per CU) issues 8 * iters
  * independent v_mfma_scale_f32_32x32x64_f8f6f4 per wave, with FP8 operands

@@ -130,6 +130,21 @@ def test_oversize_operands_are_refused():
              None) == bq.SVDQ_ERR_SHAPE
 
 
+def test_noalloc_validates_and_refuses_beyond_its_array():
+    """The no-allocation unfused call: NULL / misaligned pointers, MXFP4,
+    and a layer whose intermediates exceed the library's 32 MiB device array
+    (M = 4608, K = 16384: 36 MiB of codes) -> SVDQ_ERR_SHAPE, before any
+    device work."""
+    f = bq.lib.svdq_unfused_linear_noalloc
+    assert bq.NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert f(None, 16, 64, FAKE, FAKE, 16, FAKE, FAKE, FAKE, None, 16, 0, FAKE, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert f(FAKE, 16, 64, FAKE, FAKE, 16, FAKE, FAKE, FAKE, MIS, 16, 0, FAKE, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert f(FAKE, 16, 128, FAKE, FAKE, 16, FAKE, FAKE, FAKE, None, 16, bq.MXFP4, FAKE, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert f(FAKE, 4608, 16384, FAKE, FAKE, 32, FAKE, FAKE, FAKE, None, 64, 0, FAKE, None) == bq.SVDQ_ERR_SHAPE
+    # FLUX fc2 (4608 x 12288, rank 32) fits: it stops at the device check here, not at the size
+    assert f(FAKE, 4608, 12288, FAKE, FAKE, 32, FAKE, FAKE, FAKE, None, 64, 0, FAKE, None) != bq.SVDQ_ERR_SHAPE
+
+
 def test_mlp_calls_validate():
     """The GELU and fused-MLP calls: NULL / misaligned pointers, MXFP4
     (INT4 only), N not a multiple of 128 for the fused pair, rank rules."""
