@@ -24,6 +24,7 @@
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -100,6 +101,54 @@ constexpr int kQuantNone = 0, kQuantInt4 = 1, kQuantMx = 2;
 // Bits of 2^e as fp32 for e in [-127, 127] (2^-127 is a subnormal).
 __device__ __forceinline__ float exp2i_f32(int e) {
   return e >= -126 ? __uint_as_float(static_cast<uint32_t>(e + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+// ---------------------------------------------------------------------------
+// INT4 code layout (shared by kernel 1, the fused MLP tail and the GEMMs).
+//
+// A unit of 16 consecutive k is two little-endian words I0, I1.  Code q has
+// the 6-bit image 32 [q < 0] + |q|, which is the FP6 E2M3 pattern of q/8
+// (bits 3-4, the exponent, are zero: a subnormal); image j of the unit sits
+// at bits 6j..6j+5 of the 96-bit string D0 | D1 << 32 | D2 << 64, the
+// layout in which the matrix core reads 16 FP6 values from three VGPRs.
+// Stored: I0 = D0 | (D2 & kZ0), I1 = D1 | (D2 & kZ1) -- the masks are the
+// zero exponent bits of the images in D0 and D1, which together are exactly
+// the data bits of D2 -- so the matrix-core words come back with four
+// operations per unit: D0 = I0 & ~kZ0, D1 = I1 & ~kZ1,
+// D2 = (I0 & kZ0) | (I1 & kZ1).
+// ---------------------------------------------------------------------------
+constexpr uint32_t kZ0 = 0x18618618u;     // bits 3,4 9,10 15,16 21,22 27,28
+constexpr uint32_t kZ1 = 0x86186186u;     // bits 1,2 7,8 13,14 19,20 25,26 31
+
+typedef __bf16 v32bf __attribute__((ext_vector_type(32)));
+typedef unsigned v6u __attribute__((ext_vector_type(6)));
+typedef float v32f __attribute__((ext_vector_type(32)));
+
+// 32 values (x[c][e] = value 8c + e) -> their INT4 codes in the code layout,
+// q = clamp(rint(fp32(x * inv)), -7, 7) with ties to even, as 16 bytes (two
+// units).  invs = inv / 8 (exact), so v = x * invs is fp32(x * inv) / 8 and
+// (v + 1.5 * 2^20) - 1.5 * 2^20 rounds it to the 1/8 grid with ties to even
+// -- q/8 -- and gives +0 for a negative value that rounds to zero; clamped
+// to +-7/8 it is exact in bf16, and v_cvt_scalef32_pk32_fp6_bf16 (scale 1)
+// writes the 32 values as FP6 images in order, D0..D5.
+__device__ __forceinline__ uint4 pack_codes_fp6(const float (&x)[4][8], float invs) {
+#pragma clang fp contract(off)
+  constexpr float kMagic = 1572864.0f;           // 1.5 * 2^20: ulp 1/8 on [2^20, 2^21)
+  v32bf h;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      float r0 = (x[c][e] * invs + kMagic) - kMagic;
+      float r1 = (x[c][e + 1] * invs + kMagic) - kMagic;
+      r0 = __builtin_amdgcn_fmed3f(r0, -0.875f, 0.875f);
+      r1 = __builtin_amdgcn_fmed3f(r1, -0.875f, 0.875f);
+      const v2bf b = __builtin_convertvector((v2f{r0, r1}), v2bf);
+      h[8 * c + e] = b[0];
+      h[8 * c + e + 1] = b[1];
+    }
+  const v6u d = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(h, 1.0f);
+  return make_uint4(d[0] | (d[2] & kZ0), d[1] | (d[2] & kZ1), d[3] | (d[5] & kZ0), d[4] | (d[5] & kZ1));
 }
 
 template <int RT, bool ATOMIC, int QMODE = kQuantInt4>
@@ -257,36 +306,10 @@ __global__ __launch_bounds__(256) void k1_quant_down_int4(
       const uint32_t sbits = f16_sat_bits(__fdiv_rn(amax, 7.0f));
       const float s = f16_bits_to_f32(sbits);
       const float inv = (s == 0.f) ? 0.f : __fdiv_rn(1.0f, s);
-      // 8 codes per word: each code as the byte s000_0mmm (sign of a
-      // negative code in bit 7, |q| in bits 0-2), E = the even-k bytes,
-      // O = the odd-k bytes, word = E | rotl32(O, 4).  That byte is the FP8
-      // E4M3 image of q * 2^-9, so v_cvt_pk_fp8_f32 of fp32(x^ * inv) * 2^-9
-      // (exact: a power of two), clamped to +-7 * 2^-9 first, rounds to the
-      // nearest code with ties to the even one -- the rint of the rule.  A
-      // value that rounds to zero keeps no sign.
-      const float invs = inv * 0x1p-9f;
-      constexpr float kLim = 7.0f * 0x1p-9f;
-      auto unsign_zero = [](uint32_t w) {
-        const uint32_t mag = w & 0x07070707u;
-        return mag | (w & ((mag + 0x7F7F7F7Fu) & 0x80808080u));
-      };
-      uint32_t word[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = fminf(kLim, fmaxf(-kLim, xh[c][e] * invs));
-        int ew = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[2], 0, false);
-        ew = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[6], ew, true);
-        int ow = __builtin_amdgcn_cvt_pk_fp8_f32(v[1], v[3], 0, false);
-        ow = __builtin_amdgcn_cvt_pk_fp8_f32(v[5], v[7], ow, true);
-        const uint32_t E = unsign_zero(static_cast<uint32_t>(ew));
-        const uint32_t O = unsign_zero(static_cast<uint32_t>(ow));
-        word[c] = E | __builtin_amdgcn_alignbit(O, O, 28);
-      }
-      // the lane's 32 codes are 16 contiguous bytes of the packed row
-      if (row_ok && valid)
-        *reinterpret_cast<uint4*>(xq + xrow / 2 + (kbase + q * 32) / 2) = make_uint4(word[0], word[1], word[2], word[3]);
+      // the lane's 32 codes are 16 contiguous bytes of the packed row: two
+      // units of 16 codes in the layer's code layout (pack_codes_fp6)
+      const uint4 packed = pack_codes_fp6(xh, inv * 0.125f);
+      if (row_ok && valid) *reinterpret_cast<uint4*>(xq + xrow / 2 + (kbase + q * 32) / 2) = packed;
       if (row_ok && valid && (q & 1) == 0) xs[static_cast<size_t>(g) * M + row] = static_cast<uint16_t>(sbits);
     } else if constexpr (QMODE == kQuantMx) {
       // MXFP4 (OCP MX): the lane's 32 k are one block.  e = floor(log2
@@ -392,13 +415,12 @@ __global__ void fill_zero_f32(float* __restrict__ p, size_t n) {
 // channels of one token; the epilogue turns the tile around in LDS so that
 // Y is written in 16-byte row segments.
 //
-// INT4 codes reach the matrix core as FP8 E4M3 subnormals: a code q becomes
-// the byte s000_0mmm (sign, |q|), which is exactly q * 2^-9; the packed
-// layout keeps those bytes two masks away (unpack_store_fp8).  For
-// one K-group of 64, v_mfma_scale_f32_32x32x64_f8f6f4 then returns the
-// group's integer partial P times 2^-18 times its two E8M0 block scales,
-// exactly: every product is a multiple of 2^-18 and every partial sum stays
-// below 2^24 of those units.  MXFP4 codes are the matrix core's own FP4.
+// INT4 codes reach the matrix core as FP6 E2M3 values q/8 (the code
+// layout is built for that: four operations per 16 codes recover the
+// matrix core's words); for one K-group of 64,
+// v_mfma_scale_f32_32x32x64_f8f6f4 then returns the group's integer partial
+// P / 64 times its two E8M0 block scales, exactly.  MXFP4 codes are the
+// matrix core's own FP4.
 // ---------------------------------------------------------------------------
 
 constexpr int kTile = 128;      // output tile edge (both n and m)
@@ -451,24 +473,6 @@ __device__ __forceinline__ TileCoord tile_coord(int pid, int tiles_n, int tiles_
   return tc;
 }
 
-// 16 packed bytes (32 codes) -> 32 FP8 E4M3 bytes.  A packed word is
-// E | rotl32(O, 4) with E and O the FP8 images (s000_0mmm) of its 4 even-k
-// and 4 odd-k codes, so E = w & 0x87878787 and O = rotr32(w, 4) &
-// 0x87878787.  E goes to one output dword and O to the next: a fixed
-// permutation of k that A and B share.
-__device__ __forceinline__ void unpack_store_fp8(int8_t* dst, const uint4& w) {
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-  uint32_t o[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    o[2 * i] = ws[i] & 0x87878787u;
-    o[2 * i + 1] = __builtin_amdgcn_alignbit(ws[i], ws[i], 4) & 0x87878787u;
-  }
-  uint4* d = reinterpret_cast<uint4*>(dst);
-  d[0] = make_uint4(o[0], o[1], o[2], o[3]);
-  d[1] = make_uint4(o[4], o[5], o[6], o[7]);
-}
-
 // ---------------------------------------------------------------------------
 // Kernel 2, MXFP4: FP4 GEMM with E8M0 block scales + up projection + bias.
 //
@@ -504,6 +508,16 @@ constexpr int kMxThreads = 256;
 constexpr int kMxYRow = kTile + 8;               // staging row stride of the output tile (bf16 elements)
 static_assert(2 * kMxSlot >= kTile * kMxYRow * 2, "output staging fits in the ring");
 
+// The staged 128-row output tile of the epilogue: rows 0-63 at lo, rows
+// 64-127 at hi, kMxYRow bf16 per row (the halves may sit in different LDS
+// arrays).
+struct StageTile {
+  uint16_t* lo;
+  uint16_t* hi;
+  __device__ __forceinline__ uint16_t* row(int r) const { return r < 64 ? lo + r * kMxYRow : hi + (r - 64) * kMxYRow; }
+};
+__device__ __forceinline__ StageTile stage_tile(uint16_t* base) { return StageTile{base, base + 64 * kMxYRow}; }
+
 // tanh-form GELU, 0.5 y (1 + tanh(u)) with u = sqrt(2/pi) (y + 0.044715 y^3),
 // evaluated as y / (1 + exp(-2u)) with the hardware exp2 and reciprocal
 // (relative error a few ulp of fp32).
@@ -526,20 +540,15 @@ struct MlpOut {
 
 // The second layer's kernel 1 on a staged 128 x 128 tile of X2 (bf16,
 // [m][n] with row stride kMxYRow); N % 128 == 0.
-__device__ __forceinline__ void mlp_tail(uint16_t* __restrict__ stg, int M, int N, int n0, int m0, int tid,
+__device__ __forceinline__ void mlp_tail(const StageTile& stg, int M, int N, int n0, int m0, int tid,
                                          const MlpOut& mo) {
   // thread t owns one 64-column group of one tile row: row t/2, columns
   // 64 (t%2) .. +64, so the group's absmax and scale stay in its registers
   const int r = tid >> 1, c0 = (tid & 1) * 64;
   const int m = m0 + r;
   const size_t rowb2 = static_cast<size_t>(N / 2);
-  constexpr float kLim = 7.0f * 0x1p-9f;
-  auto unsign_zero = [](uint32_t w) {
-    const uint32_t mag = w & 0x07070707u;
-    return mag | (w & ((mag + 0x7F7F7F7Fu) & 0x80808080u));
-  };
-  uint16_t* srow = stg + r * kMxYRow + c0;
-  float xh[64];
+  uint16_t* srow = stg.row(r) + c0;
+  float xh[2][4][8];            // the group's 64 values: two halves of 32 (the code layout's 16-byte runs)
   float amax = 0.f;
 #pragma unroll
   for (int ch = 0; ch < 8; ++ch) {
@@ -552,33 +561,21 @@ __device__ __forceinline__ void mlp_tail(uint16_t* __restrict__ stg, int M, int 
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       p[e] = cvt_pk_bf16(__uint_as_float(w4[e] << 16) * sv[2 * e], __uint_as_float(w4[e] & 0xFFFF0000u) * sv[2 * e + 1]);
-      xh[8 * ch + 2 * e] = __uint_as_float(p[e] << 16);
-      xh[8 * ch + 2 * e + 1] = __uint_as_float(p[e] & 0xFFFF0000u);
-      amax = fmaxf(amax, fmaxf(fabsf(xh[8 * ch + 2 * e]), fabsf(xh[8 * ch + 2 * e + 1])));
+      xh[ch >> 2][ch & 3][2 * e] = __uint_as_float(p[e] << 16);
+      xh[ch >> 2][ch & 3][2 * e + 1] = __uint_as_float(p[e] & 0xFFFF0000u);
+      amax = fmaxf(amax, fmaxf(fabsf(xh[ch >> 2][ch & 3][2 * e]), fabsf(xh[ch >> 2][ch & 3][2 * e + 1])));
     }
     *reinterpret_cast<uint4*>(srow + 8 * ch) = make_uint4(p[0], p[1], p[2], p[3]);   // x^2 for the MFMA
   }
   const uint32_t sbits = f16_sat_bits(__fdiv_rn(amax, 7.0f));
   const float sc = f16_bits_to_f32(sbits);
-  const float invs = ((sc == 0.f) ? 0.f : __fdiv_rn(1.0f, sc)) * 0x1p-9f;
-  uint32_t words[8];
-#pragma unroll
-  for (int ch = 0; ch < 8; ++ch) {
-    float qv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qv[e] = fminf(kLim, fmaxf(-kLim, xh[8 * ch + e] * invs));
-    int ew = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[2], 0, false);
-    ew = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4], qv[6], ew, true);
-    int ow = __builtin_amdgcn_cvt_pk_fp8_f32(qv[1], qv[3], 0, false);
-    ow = __builtin_amdgcn_cvt_pk_fp8_f32(qv[5], qv[7], ow, true);
-    const uint32_t E = unsign_zero(static_cast<uint32_t>(ew));
-    const uint32_t O = unsign_zero(static_cast<uint32_t>(ow));
-    words[ch] = E | __builtin_amdgcn_alignbit(O, O, 28);
-  }
+  const float invs = ((sc == 0.f) ? 0.f : __fdiv_rn(1.0f, sc)) * 0.125f;
+  const uint4 w0 = pack_codes_fp6(xh[0], invs);
+  const uint4 w1 = pack_codes_fp6(xh[1], invs);
   if (m < M) {
     uint4* dst = reinterpret_cast<uint4*>(mo.xq2 + static_cast<size_t>(m) * rowb2 + (n0 + c0) / 2);
-    dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
-    dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
+    dst[0] = w0;
+    dst[1] = w1;
     mo.xs2[static_cast<size_t>((n0 + c0) / 64) * M + m] = static_cast<uint16_t>(sbits);
   }
   __syncthreads();
@@ -594,7 +591,7 @@ __device__ __forceinline__ void mlp_tail(uint16_t* __restrict__ stg, int M, int 
       const v4i b = *reinterpret_cast<const v4i*>(mo.ldown2 + static_cast<size_t>(rt * 16 + r16) * N + n0 + 32 * ks + 8 * qq);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const v4i a = *reinterpret_cast<const v4i*>(stg + (32 * wave + 16 * mt + r16) * kMxYRow + 32 * ks + 8 * qq);
+        const v4i a = *reinterpret_cast<const v4i*>(stg.row(32 * wave + 16 * mt + r16) + 32 * ks + 8 * qq);
         d[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), d[mt],
                                                        0, 0, 0);
       }
@@ -636,7 +633,7 @@ __device__ __forceinline__ void mlp_tail(uint16_t* __restrict__ stg, int M, int 
 // at byte 16384, 64-byte rows, chunk c of row r at c ^ ((r / 4) % 4)) are
 // already in LDS at upl.
 template <int EPI, bool UPL = false>
-__device__ __forceinline__ void epilogue_tile128(v16f (&acc)[2][2], uint16_t* __restrict__ stg,
+__device__ __forceinline__ void epilogue_tile128(v16f (&acc)[2][2], const StageTile& stg,
                                                  const float* __restrict__ lact, const uint16_t* __restrict__ lup,
                                                  const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M,
                                                  int N, int rank, int n0, int m0, int wn, int wm, int l32, int h,
@@ -735,7 +732,7 @@ __device__ __forceinline__ void epilogue_tile128(v16f (&acc)[2][2], uint16_t* __
           p01 = cvt_pk_bf16(gelu_tanh_f32(__uint_as_float(p01 << 16)), gelu_tanh_f32(__uint_as_float(p01 & 0xFFFF0000u)));
           p23 = cvt_pk_bf16(gelu_tanh_f32(__uint_as_float(p23 << 16)), gelu_tanh_f32(__uint_as_float(p23 & 0xFFFF0000u)));
         }
-        *reinterpret_cast<uint2*>(stg + ml * kMxYRow + nl) = make_uint2(p01, p23);
+        *reinterpret_cast<uint2*>(stg.row(ml) + nl) = make_uint2(p01, p23);
       }
   __syncthreads();
 
@@ -752,7 +749,7 @@ __device__ __forceinline__ void epilogue_tile128(v16f (&acc)[2][2], uint16_t* __
     const int r = (tid >> 4) + 16 * i;
     const int m = m0 + r;
     if (m < M && n < N) {
-      const uint4 v = *reinterpret_cast<const uint4*>(stg + r * kMxYRow + c8);
+      const uint4 v = *reinterpret_cast<const uint4*>(stg.row(r) + c8);
       uint16_t* dst = y + static_cast<size_t>(m) * N + n;
       if ((N % 8) == 0) {
         *reinterpret_cast<uint4*>(dst) = v;
@@ -950,35 +947,69 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_mxfp4(
 
   const int last = (S - 1) & 1;
   if (upl)
-    epilogue_tile128<0, true>(acc, reinterpret_cast<uint16_t*>(&lds_c[last][0]), lact, lup, bias, y, M, N, rank, n0,
+    epilogue_tile128<0, true>(acc, stage_tile(reinterpret_cast<uint16_t*>(&lds_c[last][0])), lact, lup, bias, y, M, N, rank, n0,
                               m0, wn, wm, l32, h, tid, MlpOut{}, &lds_c[1 - last][0]);
   else
-    epilogue_tile128<0>(acc, reinterpret_cast<uint16_t*>(&lds_c[0][0]), lact, lup, bias, y, M, N, rank, n0, m0, wn,
-                        wm, l32, h, tid, MlpOut{});
+    epilogue_tile128<0>(acc, stage_tile(reinterpret_cast<uint16_t*>(&lds_c[0][0])), lact, lup, bias, y, M, N, rank, n0,
+                        m0, wn, wm, l32, h, tid, MlpOut{});
 }
 
 // Kernel 2, INT4: 4-bit GEMM + per-group dequant + up projection + bias.
 //
-// Same tiling, two-slot pipeline and epilogue as the MXFP4 kernel: output
-// tile 128 (n) x 128 (m) per workgroup of 4 waves, 64 x 64 per wave.  A
-// stage is 128 k = two K-groups: per row 64 packed bytes and two fp16
-// scales.  The loader converts each 16 packed bytes to FP8 E4M3 subnormals
-// on their way into LDS (unpack_store_fp8: q * 2^-9 for the code q),
-// so that v_mfma_scale_f32_32x32x64_f8f6f4 returns the group's exact integer
-// partial P scaled by 2^(e_w + e_x) (exponents of the two scales applied as
-// E8M0 block scales, with 2^18 on the W side to cancel the code encoding).
-// The products of the scale significands (in [0.5, 1)) come from a rank-1
-// v_mfma_f32_32x32x8_f16, exact in fp32 and in P's layout, and one fp32 FMA
-// per element adds P' * (m_w m_x) into the accumulators.
+// Same tiling and epilogue as the MXFP4 kernel: output tile 128 (n) x 128
+// (m) per workgroup of 4 waves, 64 x 64 per wave.  A stage is 128 k = two
+// K-groups: per row 64 packed bytes and two fp16 scales.
 //
-// DEBUG = true is a test hook on the same loader, LDS layout and MFMA path:
-// unit scales, and the exact integer partial of every K-group written for a
-// window [win_m0, +win_mt) x [win_n0, +win_nt) of the output instead of Y.
+// Operands: the packed codes travel straight from memory into LDS
+// (buffer_load ... lds, 16 bytes per lane: no staging registers, no LDS
+// stores) through a three-slot ring, two stages ahead of their use.  Rows
+// are 64 bytes, unpadded; logical 16-byte chunk j of row r (group j/2, half
+// j%2) sits at chunk j ^ swz4(r), so that the 16-byte reads of 32
+// consecutive rows at one chunk fall in distinct banks.  Each wave reads
+// its operands' packed chunks and turns each into the six words in which
+// v_mfma_scale_f32_32x32x64_f8f6f4 reads 32 FP6 E2M3 values q/8 (four
+// operations per unit of 16 codes, see the code layout), so one FP6 MFMA
+// over a group (K = 64) returns sum qw qx / 64 = P / 64 with the two scales'
+// exponents applied as E8M0 block scales, exactly: every product is a
+// multiple of 2^-6 and |P| <= 3136.
+//
+// Dequant: a scale s = m 2^e (m in [0.5, 1), v_frexp) gives the MFMA its
+// exponent (+6 on the W side cancels the 1/64; -1 on the X side cancels
+// the doubled product below); the significand products m_w(n) m_x(m) of a
+// 32 x 32 tile-group are a rank-1 matrix, which one v_mfma_f32_32x32x8_f16
+// returns exactly in fp32 and in P's layout (both lane halves carry the
+// significands, so it comes out doubled); one fp32 FMA per element then adds
+// P' * (2 m_w m_x) into the accumulators.  The scales are split once per
+// workgroup (one row per thread) into a three-slot LDS ring of their own.
+//
+// DEBUG = true is a test hook on the same loads, LDS ring, code conversion
+// and FP6 MFMA: unit scales, and the exact integer partial of every K-group
+// written for a window [win_m0, +win_mt) x [win_n0, +win_nt) of the output
+// instead of Y.
 // ---------------------------------------------------------------------------
-constexpr int kI4Stage = 128;                 // k per pipeline stage (2 groups)
-constexpr int kI4Row = 2 * 64 + 16;           // LDS row stride: 128 FP8 codes + 16 bytes padding
-constexpr int kI4Slot = 2 * kTile * kI4Row;   // W rows, then X rows
-static_assert(2 * kI4Slot >= kTile * kMxYRow * 2, "output staging fits in the ring");
+constexpr int kI4Stage = 128;                    // k per pipeline stage (2 groups)
+constexpr int kI4RowB = kI4Stage / 2;            // packed bytes per row and stage
+constexpr int kI4Op = kTile * kI4RowB;           // one operand's rows in a slot (8 KB)
+constexpr int kI4Slots = 3;                      // ring depth: loads run two stages ahead
+// every slot's W rows and X rows are LDS arrays of their own (so that the
+// compiler tells a stage's reads from the loads landing in another slot and
+// waits for neither); slot 0's two arrays also hold the epilogue's output
+// tile, a half each
+constexpr int kI4Half = 64 * kMxYRow * 2;        // 64 staged output rows
+static_assert(kI4Half >= kI4Op, "slot 0's arrays hold both code rows and output rows");
+
+// chunk swizzle of a 64-byte LDS row: bits (r1 ^ r3, r2) of the row index.
+// Over any 8 consecutive rows (r0 = 0 mod 8) r mod 2 and the swizzle take all
+// 8 combinations, and over any 16 (r0 = 0 mod 16) r mod 4 and the swizzle
+// take all 16: conflict-free 16-byte reads for 32 and for 64 four-byte banks.
+__device__ __forceinline__ int swz4(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | ((r >> 1) & 2); }
+
+// one packed chunk (two units, 32 codes) -> the six matrix-core words
+__device__ __forceinline__ v8i fp6_words(const uint4& w) {
+  return v8i{static_cast<int>(w.x & ~kZ0), static_cast<int>(w.y & ~kZ1), static_cast<int>((w.x & kZ0) | (w.y & kZ1)),
+             static_cast<int>(w.z & ~kZ0), static_cast<int>(w.w & ~kZ1), static_cast<int>((w.z & kZ0) | (w.w & kZ1)),
+             0, 0};
+}
 
 template <bool DEBUG, int EPI = 0>
 __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
@@ -987,11 +1018,24 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
     const float* __restrict__ lact, const uint16_t* __restrict__ lup,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N, int K, int rank,
     int win_m0, int win_n0, int win_mt, int win_nt, int32_t* __restrict__ dbg, MlpOut mo) {
-  __shared__ __attribute__((aligned(16))) int8_t lds_c[2][kI4Slot];
-  // per slot, operand (0 = W, 1 = X), group of the stage and row: the fp16
-  // significand of the scale (bits 0-15) and its E8M0 exponent byte (bits
-  // 16-23)
-  __shared__ __attribute__((aligned(16))) uint32_t lds_s[2][2][2][kTile];
+  __shared__ __attribute__((aligned(16))) uint8_t w_ring0[kI4Half];
+  __shared__ __attribute__((aligned(16))) uint8_t x_ring0[kI4Half];
+  __shared__ __attribute__((aligned(16))) uint8_t w_ring1[kI4Op];
+  __shared__ __attribute__((aligned(16))) uint8_t x_ring1[kI4Op];
+  __shared__ __attribute__((aligned(16))) uint8_t w_ring2[kI4Op];
+  __shared__ __attribute__((aligned(16))) uint8_t x_ring2[kI4Op];
+  auto wring = [&](int slot) __attribute__((always_inline)) { return slot == 0 ? w_ring0 : slot == 1 ? w_ring1 : w_ring2; };
+  auto xring = [&](int slot) __attribute__((always_inline)) { return slot == 0 ? x_ring0 : slot == 1 ? x_ring1 : x_ring2; };
+  // per slot, operand and row: the scale words of the stage's two groups
+  // {g0 word0, g0 word1, g1 word0, g1 word1} (sstore)
+  __shared__ __attribute__((aligned(16))) uint4 ws_ring0[kTile];
+  __shared__ __attribute__((aligned(16))) uint4 xs_ring0[kTile];
+  __shared__ __attribute__((aligned(16))) uint4 ws_ring1[kTile];
+  __shared__ __attribute__((aligned(16))) uint4 xs_ring1[kTile];
+  __shared__ __attribute__((aligned(16))) uint4 ws_ring2[kTile];
+  __shared__ __attribute__((aligned(16))) uint4 xs_ring2[kTile];
+  auto wsring = [&](int slot) __attribute__((always_inline)) { return slot == 0 ? ws_ring0 : slot == 1 ? ws_ring1 : ws_ring2; };
+  auto xsring = [&](int slot) __attribute__((always_inline)) { return slot == 0 ? xs_ring0 : slot == 1 ? xs_ring1 : xs_ring2; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1001,7 +1045,7 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   const int wn = wave >> 1, wm = wave & 1;
   const int G = K / 64;
   const int S = (G + 1) / 2;                   // the last stage holds one group when G is odd
-  const size_t kb = static_cast<size_t>(K / 2);
+  const int kb = K / 2;
 
   int n0, m0;
   if constexpr (DEBUG) {
@@ -1014,92 +1058,81 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
     m0 = tc.m0;
   }
 
-  // Loads go through buffer resources based at the tile's first row (and at
-  // the scale array), so that a stage needs no address arithmetic: a fixed
-  // per-lane offset plus the stage's offset in a scalar register.  Every
-  // access stays inside the resource's range by construction.
-  // code loads: rows wave*32 + 16i + lane/4 (i = 0, 1) of W and X, 16-byte
-  // chunk lane%4 of the stage's 64 bytes; rows clamped into the matrix
-  const int lr = wave * 32 + (lane >> 2), lc = lane & 3;
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wq + static_cast<size_t>(n0) * kb, static_cast<size_t>(N - n0) * kb);
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(xq + static_cast<size_t>(m0) * kb, static_cast<size_t>(M - m0) * kb);
-  const int vw0 = min(lr, N - 1 - n0) * static_cast<int>(kb) + lc * 16;
-  const int vw1 = min(lr + 16, N - 1 - n0) * static_cast<int>(kb) + lc * 16;
-  const int vx0 = min(lr, M - 1 - m0) * static_cast<int>(kb) + lc * 16;
-  const int vx1 = min(lr + 16, M - 1 - m0) * static_cast<int>(kb) + lc * 16;
-  const int ldst = lr * kI4Row + lc * 32;
-  // scale loads: threads 0..127 (waves 0, 1) W, 128..255 (waves 2, 3) X;
-  // group (t/64)%2 of the stage, rows 2(t%64), 2(t%64)+1: one dword when
-  // the row count is even (pair clamped to the last two rows), else two
-  // halves from rows clamped into the matrix
+  // Code loads: waves 0, 1 load W rows, waves 2, 3 X rows, through a
+  // buffer resource based at the tile's first row.  Load j (0..3) of a wave
+  // fills rows 64 (wave % 2) + 16 j .. +15 of its operand: lane i writes LDS
+  // chunk i % 4 of row i / 4 and reads global chunk (i % 4) ^ swz4(row) of
+  // that row; rows past the matrix edge are clamped to its last row, and the
+  // resource bounds every access (a missing second group of an odd-G last
+  // stage reads zeros or the next row, never used).
+  const bool ld_w = wave < 2;                  // wave-uniform
+  const int ld_rows = ld_w ? N - n0 : M - m0;
+  const __amdgpu_buffer_rsrc_t rc =
+      make_rsrc(ld_w ? wq + static_cast<size_t>(n0) * kb : xq + static_cast<size_t>(m0) * kb,
+                static_cast<size_t>(ld_rows) * static_cast<size_t>(kb));
+  int vcode[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 64 * (wave & 1) + 16 * j + (lane >> 2);
+    vcode[j] = min(r, ld_rows - 1) * kb + (((lane & 3) ^ swz4(r)) << 4);
+  }
+  auto dma = [&](int st, int slot) __attribute__((always_inline)) {
+    const int so = st * kI4RowB;
+    if (ld_w) {
+      uint8_t* base = wring(slot) + 64 * (wave & 1) * kI4RowB;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr_t)(base + 16 * j * kI4RowB), 16, vcode[j], so, 0, 0);
+    } else {
+      uint8_t* base = xring(slot) + 64 * (wave & 1) * kI4RowB;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr_t)(base + 16 * j * kI4RowB), 16, vcode[j], so, 0, 0);
+    }
+  };
+  // Scales: thread t < 128 reads W row n0 + t, t >= 128 X row m0 + t - 128
+  // (clamped into the matrix), both groups of a stage.
   const bool s_is_w = wave < 2;                // wave-uniform
-  const int sg = wave & 1, sr = (tid & 63) * 2;
+  const int s_row = tid & (kTile - 1);
   const int s_rows = s_is_w ? N : M;
-  const int s_r0 = (s_is_w ? n0 : m0) + sr;
-  const bool s_even = (s_rows % 2) == 0;
   const __amdgpu_buffer_rsrc_t rs =
       make_rsrc(s_is_w ? ws : xs, static_cast<size_t>(G) * static_cast<size_t>(s_rows) * 2);
-  const int vs0 = 2 * (s_even ? min(s_r0, s_rows - 2) : min(s_r0, s_rows - 1));
-  const int vs1 = 2 * min(s_r0 + 1, s_rows - 1);
-  const int vsg = 2 * sg * s_rows;
-
-  struct LoadRegs {
-    uint4 w0, w1, x0, x1;
-    uint32_t s;
-  };
-  // stage st; when its second group does not exist (odd G, last stage) the
-  // lanes of that group re-read the first one (never used)
-  auto gload = [&](int st) {
-    LoadRegs L;
-    const int so = st * (kI4Stage / 2);
-    const int sso = 4 * st * s_rows;
-    int a = 0, g1 = vsg;
-    if (2 * st + 1 >= G) {
-      a = lc < 2 ? 0 : 32;
-      g1 = 0;
-    }
-    L.w0 = buffer_load_u4(rw, vw0 - a, so);
-    L.w1 = buffer_load_u4(rw, vw1 - a, so);
-    L.x0 = buffer_load_u4(rx, vx0 - a, so);
-    L.x1 = buffer_load_u4(rx, vx1 - a, so);
-    L.s = 0;
+  const int vs = 2 * min((s_is_w ? n0 : m0) + s_row, s_rows - 1);
+  const int gstride = 2 * s_rows;              // bytes per group of the scale array
+  auto sload = [&](int st) __attribute__((always_inline)) {
+    uint2 s = make_uint2(0u, 0u);
     if constexpr (!DEBUG) {
-      if (s_even) {
-        L.s = __builtin_amdgcn_raw_buffer_load_b32(rs, g1 + vs0, sso, 0);
-      } else {
-        L.s = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rs, g1 + vs0, sso, 0)) |
-              (static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rs, g1 + vs1, sso, 0)) << 16);
-      }
+      const int sso = 2 * st * gstride;
+      s.x = __builtin_amdgcn_raw_buffer_load_b16(rs, vs, sso, 0);
+      if (2 * st + 1 < G) s.y = __builtin_amdgcn_raw_buffer_load_b16(rs, vs + gstride, sso, 0);
     }
-    return L;
+    return s;
   };
-  // A scale s (fp16 >= 0) splits as s = m * 2^e with m in [0.5, 1)
-  // (v_frexp_mant_f16, v_frexp_exp_i16_f16, subnormals included): 2^e is
-  // applied exactly by the matrix core as an E8M0 block scale, m is an
-  // exact fp16.  W rows carry an extra 2^18 that cancels the 2^-18 of the
-  // FP8 code encoding; X rows carry 2^-1 that cancels the doubled outer
-  // product of the significands.  s == 0 gives m = 0; its codes are zero
-  // too.
-  auto lstore = [&](auto buf_c, LoadRegs L) {
-    constexpr int buf = decltype(buf_c)::value;
-    int8_t* wd = &lds_c[buf][0] + ldst;
-    int8_t* xd = &lds_c[buf][kTile * kI4Row] + ldst;
-    unpack_store_fp8(wd, L.w0);
-    unpack_store_fp8(wd + 16 * kI4Row, L.w1);
-    unpack_store_fp8(xd, L.x0);
-    unpack_store_fp8(xd + 16 * kI4Row, L.x1);
+  // A scale s (fp16 >= 0) splits as s = m 2^e with m in [0.5, 1)
+  // (v_frexp_mant_f16, v_frexp_exp_i16_f16, subnormals included; s == 0
+  // gives m = 0, and its codes are zero too).  Two words per row and group:
+  //   W: word0 = m | (e + 127 + 6) << 16, word1 = 0
+  //   X: word0 = m,                       word1 = (e + 127 - 1) << 16
+  // Byte 2 of W's word0 and of X's word1 is the E8M0 scale of the FP6 MFMA
+  // (op_sel 2); as f16 operands of the rank-1 MFMA ({word0, word1} = k 0-3,
+  // the same in k 4-7) W gives [m_w, e_w, 0, 0] and X [m_x, 0, 0, e_x], so
+  // only k 0 and k 4 contribute: 2 m_w m_x, exactly.
+  auto sstore = [&](int slot, const uint2& s) __attribute__((always_inline)) {
     if constexpr (DEBUG) return;
-    uint32_t eb[2];
-    _Float16 sm[2];
+    uint32_t wv[4];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const _Float16 sv = __builtin_bit_cast(_Float16, static_cast<uint16_t>(L.s >> (16 * i)));
-      eb[i] = static_cast<uint32_t>(__builtin_amdgcn_frexp_exph(sv) + (s_is_w ? 127 + 18 : 127 - 1)) & 0xFFu;
-      sm[i] = __builtin_amdgcn_frexp_manth(sv);
+      const _Float16 sv = __builtin_bit_cast(_Float16, static_cast<uint16_t>(i ? s.y : s.x));
+      const uint32_t m = __builtin_bit_cast(uint16_t, __builtin_amdgcn_frexp_manth(sv));
+      const uint32_t e =
+          static_cast<uint32_t>(__builtin_amdgcn_frexp_exph(sv) + (s_is_w ? 127 + 6 : 127 - 1)) & 0xFFu;
+      wv[2 * i] = s_is_w ? (m | (e << 16)) : m;
+      wv[2 * i + 1] = s_is_w ? 0u : (e << 16);
     }
-    *reinterpret_cast<uint2*>(&lds_s[buf][s_is_w ? 0 : 1][sg][sr]) =
-        make_uint2(static_cast<uint32_t>(__builtin_bit_cast(uint16_t, sm[0])) | (eb[0] << 16),
-                   static_cast<uint32_t>(__builtin_bit_cast(uint16_t, sm[1])) | (eb[1] << 16));
+    if (s_is_w)
+      wsring(slot)[s_row] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    else
+      xsring(slot)[s_row] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
   };
 
   v16f acc[2][2];
@@ -1110,65 +1143,71 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[it][jt][r] = 0.f;
 
-  // Operands of group g (0, 1) of the stage in slot buf: FP8 bytes 64g +
-  // 32h of the row for lane half h, the E8M0 exponent bytes, and the rank-1
-  // operands of the scale outer product (below).
-  struct Ops {
-    v8i a0, a1, b0, b1;
-    uint32_t ea0, ea1, eb0, eb1;
-    h4 sa0, sa1, sb0, sb1;
+  // packed chunks of group g for the lane: W rows (tiles 0, 1) and X rows
+  struct Raw {
+    uint4 a0, a1, b0, b1;
   };
-  auto load_ops = [&](auto buf_c, auto g_c) {
-    constexpr int buf = decltype(buf_c)::value;
+  const int ch_off = swz4(l32) << 4;           // the lane's rows are l32 mod 32
+  auto load_raw = [&](int slot, auto g_c) __attribute__((always_inline)) {
     constexpr int g = decltype(g_c)::value;
-    Ops o;
-    const int8_t* wr = &lds_c[buf][0] + (wn * 64 + l32) * kI4Row + 64 * g + 32 * h;
-    const int8_t* xr = &lds_c[buf][kTile * kI4Row] + (wm * 64 + l32) * kI4Row + 64 * g + 32 * h;
-    auto rd = [](const int8_t* q) {
-      return __builtin_shufflevector(*reinterpret_cast<const v4i*>(q), *reinterpret_cast<const v4i*>(q + 16), 0, 1, 2,
-                                     3, 4, 5, 6, 7);
-    };
-    o.a0 = rd(wr);
-    o.a1 = rd(wr + 32 * kI4Row);
-    o.b0 = rd(xr);
-    o.b1 = rd(xr + 32 * kI4Row);
-    // one word per row: the exponent byte goes to the MFMA as byte 2
-    // (op_sel 2), the significand (bits 0-15) to the outer product
-    o.ea0 = lds_s[buf][0][g][wn * 64 + l32];
-    o.ea1 = lds_s[buf][0][g][wn * 64 + 32 + l32];
-    o.eb0 = lds_s[buf][1][g][wm * 64 + l32];
-    o.eb1 = lds_s[buf][1][g][wm * 64 + 32 + l32];
-    // outer-product operands: k 0 (lanes 0-31) and k 4 (lanes 32-63) both
-    // carry the significand, so the product comes out doubled (exactly;
-    // the X exponent byte is one lower to cancel it); the W word's exponent
-    // byte lands in k 1 / k 5, where the X operand is zero
-    o.sa0 = __builtin_bit_cast(h4, make_uint2(o.ea0, 0u));
-    o.sa1 = __builtin_bit_cast(h4, make_uint2(o.ea1, 0u));
-    o.sb0 = __builtin_bit_cast(h4, make_uint2(o.eb0 & 0xFFFFu, 0u));
-    o.sb1 = __builtin_bit_cast(h4, make_uint2(o.eb1 & 0xFFFFu, 0u));
+    const int off = ((2 * g + h) << 4) ^ ch_off;
+    const uint8_t* wr = wring(slot) + (wn * 64 + l32) * kI4RowB + off;
+    const uint8_t* xr = xring(slot) + (wm * 64 + l32) * kI4RowB + off;
+    Raw o;
+    o.a0 = *reinterpret_cast<const uint4*>(wr);
+    o.a1 = *reinterpret_cast<const uint4*>(wr + 32 * kI4RowB);
+    o.b0 = *reinterpret_cast<const uint4*>(xr);
+    o.b1 = *reinterpret_cast<const uint4*>(xr + 32 * kI4RowB);
     return o;
   };
-  // tile-group t = 2 it + jt: the group's partial P of W tile it and X
-  // tile jt, times 2^(e_w + e_x) (exact)
-  auto mf2 = [&](const Ops& o, auto t_c) {
+  struct Ops {
+    v8i a0, a1, b0, b1;
+  };
+  auto cvt = [&](const Raw& r) __attribute__((always_inline)) {
+    Ops o;
+    o.a0 = fp6_words(r.a0);
+    o.a1 = fp6_words(r.a1);
+    o.b0 = fp6_words(r.b0);
+    o.b1 = fp6_words(r.b1);
+    return o;
+  };
+  // the stage's scale words of the lane's W rows (tiles 0, 1) and X rows
+  struct Scl {
+    uint4 w0, w1, x0, x1;
+  };
+  auto load_scl = [&](int slot) __attribute__((always_inline)) {
+    Scl c;
+    c.w0 = wsring(slot)[wn * 64 + l32];
+    c.w1 = wsring(slot)[wn * 64 + 32 + l32];
+    c.x0 = xsring(slot)[wm * 64 + l32];
+    c.x1 = xsring(slot)[wm * 64 + 32 + l32];
+    return c;
+  };
+  // tile-group t = 2 it + jt of group g: the partial P of W tile it and X
+  // tile jt, times 2^(e_w + e_x) / 2 (exact)
+  auto mf = [&](const Ops& o, const Scl& c, auto g_c, auto t_c) __attribute__((always_inline)) {
+    constexpr int g = decltype(g_c)::value;
     constexpr int t = decltype(t_c)::value;
     constexpr int it = t >> 1, jt = t & 1;
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(it ? o.a1 : o.a0, jt ? o.b1 : o.b0, v16f{}, 0, 0, 2,
-                                                           it ? o.ea1 : o.ea0, 2, jt ? o.eb1 : o.eb0);
+    const uint4& sw = it ? c.w1 : c.w0;
+    const uint4& sx = jt ? c.x1 : c.x0;
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(it ? o.a1 : o.a0, jt ? o.b1 : o.b0, v16f{}, 2, 2, 2,
+                                                           static_cast<int>(g ? sw.z : sw.x), 2,
+                                                           static_cast<int>(g ? sx.w : sx.y));
   };
-  // Scale outer product of tile-group t.  The products m_w(n) m_x(m) of
-  // the scale significands form a rank-1 32 x 32 matrix:
-  // v_mfma_f32_32x32x8_f16 with k 0 and k 4 holding m_w (A) and m_x (B)
-  // returns it, doubled, exactly in fp32 and in the accumulator layout of P
-  // (the doubling is cancelled by the X exponent), so that the dequant
-  // (dqc) is one fp32 FMA per element on the VALU.
+  // the rank-1 product 2 m_w m_x of the same tile-group
   const v16f zero16 = {};
-  auto rk = [&](const Ops& o, auto t_c) {
+  auto rk = [&](const Scl& c, auto g_c, auto t_c) __attribute__((always_inline)) {
+    constexpr int g = decltype(g_c)::value;
     constexpr int t = decltype(t_c)::value;
     constexpr int it = t >> 1, jt = t & 1;
-    return __builtin_amdgcn_mfma_f32_32x32x8f16(it ? o.sa1 : o.sa0, jt ? o.sb1 : o.sb0, zero16, 0, 0, 0);
+    const uint4& sw = it ? c.w1 : c.w0;
+    const uint4& sx = jt ? c.x1 : c.x0;
+    const h4 a = __builtin_bit_cast(h4, g ? make_uint2(sw.z, sw.w) : make_uint2(sw.x, sw.y));
+    const h4 b = __builtin_bit_cast(h4, g ? make_uint2(sx.z, sx.w) : make_uint2(sx.x, sx.y));
+    return __builtin_amdgcn_mfma_f32_32x32x8f16(a, b, zero16, 0, 0, 0);
   };
-  auto dqc = [&](auto t_c, const v16f& p, const v16f& c) {
+  auto dqc = [&](auto t_c, const v16f& p, const v16f& c) __attribute__((always_inline)) {
     constexpr int t = decltype(t_c)::value;
     constexpr int it = t >> 1, jt = t & 1;
 #pragma unroll
@@ -1180,36 +1219,34 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   using I3 = Slot<3>;
 
   // A stage (one group on an odd-G last stage) as one software pipeline
-  // over its tile-groups: both MFMAs of tile-group t+1 (the FP8 product and
+  // over its tile-groups: both MFMAs of tile-group t+1 (the FP6 product and
   // the scale outer product) are issued before the dequant of tile-group t,
-  // so the FMAs find their operands done; the second group's operands are
-  // read while the first group computes.  DEBUG: unit scales, and the exact integer
-  // partial of every group written for the window instead.
-  // the stage's last two tile-groups (it = 1) leave compute with their
-  // MFMAs in flight; their dequant (finish) runs after the stage barrier
+  // so the FMAs find their operands done; the second group's chunks are read
+  // and converted while the first group computes.  The stage's last two
+  // tile-groups leave compute with their MFMAs in flight; their dequant
+  // (finish) runs after the stage barrier.
   v16f pa, pb, ca, cb;
-  auto finish = [&]() {
+  auto finish = [&]() __attribute__((always_inline)) {
     dqc(I2{}, pa, ca);
     dqc(I3{}, pb, cb);
   };
-  auto compute = [&](auto buf_c, bool one, int g0) {
+  auto compute = [&](int slot, bool one, int g0) __attribute__((always_inline)) {
     if constexpr (DEBUG) {
-      auto group = [&](auto g_c) {
+      auto group = [&](auto g_c) __attribute__((always_inline)) {
         constexpr int g = decltype(g_c)::value;
-        const Ops o = load_ops(buf_c, g_c);
+        const Ops o = cvt(load_raw(slot, g_c));
         const v8i a[2] = {o.a0, o.a1}, b[2] = {o.b0, o.b1};
 #pragma unroll
         for (int it = 0; it < 2; ++it)
 #pragma unroll
           for (int jt = 0; jt < 2; ++jt) {
-            const v16f p =
-                __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[it], b[jt], v16f{}, 0, 0, 0, kUnitScales, 0,
-                                                                kUnitScales);
+            const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[it], b[jt], v16f{}, 2, 2, 0,
+                                                                           kUnitScales, 0, kUnitScales);
             int32_t pi[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              pi[r] = static_cast<int32_t>(p[r] * 262144.0f);     // exact: P * 2^-18 * 2^18
-              asm volatile("" : "+v"(pi[r]));                    // read the MFMA result before the predicated stores
+              pi[r] = static_cast<int32_t>(p[r] * 64.0f);     // exact: P / 64 * 64
+              asm volatile("" : "+v"(pi[r]));               // read the MFMA result before the predicated stores
             }
             const int m = m0 + wm * 64 + jt * 32 + l32;
 #pragma unroll
@@ -1223,57 +1260,84 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
       group(I0{});
       if (!one) group(I1{});
     } else {
-      const Ops o0 = load_ops(buf_c, I0{});
-      pa = mf2(o0, I0{});
-      pb = mf2(o0, I1{});
-      ca = rk(o0, I0{});
-      cb = rk(o0, I1{});
+      const Raw r0 = load_raw(slot, I0{});
+      const Scl c = load_scl(slot);
+      const Ops o0 = cvt(r0);
+      pa = mf(o0, c, I0{}, I0{});
+      ca = rk(c, I0{}, I0{});
+      pb = mf(o0, c, I0{}, I1{});
+      cb = rk(c, I0{}, I1{});
       dqc(I0{}, pa, ca);
-      pa = mf2(o0, I2{});
-      ca = rk(o0, I2{});
+      pa = mf(o0, c, I0{}, I2{});
+      ca = rk(c, I0{}, I2{});
       dqc(I1{}, pb, cb);
-      pb = mf2(o0, I3{});
-      cb = rk(o0, I3{});
+      pb = mf(o0, c, I0{}, I3{});
+      cb = rk(c, I0{}, I3{});
       if (one) return;
-      const Ops o1 = load_ops(buf_c, I1{});
+      const Ops o1 = cvt(load_raw(slot, I1{}));
       dqc(I2{}, pa, ca);
-      pa = mf2(o1, I0{});
-      ca = rk(o1, I0{});
+      pa = mf(o1, c, I1{}, I0{});
+      ca = rk(c, I1{}, I0{});
       dqc(I3{}, pb, cb);
-      pb = mf2(o1, I1{});
-      cb = rk(o1, I1{});
+      pb = mf(o1, c, I1{}, I1{});
+      cb = rk(c, I1{}, I1{});
       dqc(I0{}, pa, ca);
-      pa = mf2(o1, I2{});
-      ca = rk(o1, I2{});
+      pa = mf(o1, c, I1{}, I2{});
+      ca = rk(c, I1{}, I2{});
       dqc(I1{}, pb, cb);
-      pb = mf2(o1, I3{});
-      cb = rk(o1, I3{});
+      pb = mf(o1, c, I1{}, I3{});
+      cb = rk(c, I1{}, I3{});
     }
   };
 
-  LoadRegs ld = gload(0);
-  lstore(Slot<0>{}, ld);
-  if (S > 1) ld = gload(1);
-  __syncthreads();
-
-  auto iteration = [&](int st, auto buf_c) {
-    constexpr int buf = decltype(buf_c)::value;
-    if (st + 1 < S) lstore(Slot<1 - buf>{}, ld);
+  // prologue: stages 0 and 1 in flight; stage 0 (codes and scales) in LDS
+  {
+    const uint2 s0 = sload(0);
+    dma(0, 0);
+    if (S > 1) {
+      const uint2 s1 = sload(1);
+      dma(1, 1);
+      sstore(0, s0);
+      sstore(1, s1);
+    } else {
+      sstore(0, s0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
+    __syncthreads();
+  }
+  // the ring slot of each stage is a compile-time constant (loop unrolled by
+  // three), so that the compiler can tell the stage's LDS reads from the
+  // loads landing in the slot two stages ahead and waits for neither
+  auto iteration = [&](int st, auto slot_c) __attribute__((always_inline)) {
+    constexpr int slot = decltype(slot_c)::value;
+    constexpr int slot2 = (slot + 2) % kI4Slots;
+    const bool ahead = st + 2 < S;             // uniform
+    uint2 sn = make_uint2(0u, 0u);
+    if (ahead) {
+      sn = sload(st + 2);
+      dma(st + 2, slot2);
+    }
     if constexpr (!DEBUG)
       if (st > 0) finish();
-    if (st + 2 < S) ld = gload(st + 2);
-    compute(buf_c, 2 * st + 1 >= G, 2 * st);
+    compute(slot, 2 * st + 1 >= G, 2 * st);
+    if (ahead) {
+      sstore(slot2, sn);
+      __builtin_amdgcn_s_waitcnt(0x0F74);      // vmcnt(4): only this stage's 4 code loads (stage st+2) may be out
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0)
+    }
     __syncthreads();
   };
-  for (int st = 0; st < S; st += 2) {
+  for (int st = 0; st < S; st += 3) {
     iteration(st, Slot<0>{});
     if (st + 1 < S) iteration(st + 1, Slot<1>{});
+    if (st + 2 < S) iteration(st + 2, Slot<2>{});
   }
 
   if constexpr (!DEBUG) finish();
   if constexpr (!DEBUG)
-    epilogue_tile128<EPI>(acc, reinterpret_cast<uint16_t*>(&lds_c[0][0]), lact, lup, bias, y, M, N, rank, n0, m0, wn,
-                          wm, l32, h, tid, mo);
+    epilogue_tile128<EPI>(acc, StageTile{reinterpret_cast<uint16_t*>(w_ring0), reinterpret_cast<uint16_t*>(x_ring0)}, lact,
+                          lup, bias, y, M, N, rank, n0, m0, wn, wm, l32, h, tid, mo);
 }
 
 // ---------------------------------------------------------------------------
@@ -1282,11 +1346,11 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
 //
 // Same tiling, XCD map, two-slot ring and epilogue as the 4-bit kernels; a
 // stage is one K-group of 64.  The loader turns each 16 packed bytes of W
-// into 32 bf16 weights on their way into LDS: the code words give the FP8
-// images of q * 2^-9 (E = w & 0x87878787, O = rotr32(w, 4) & 0x87878787),
-// v_cvt_pk_f32_fp8 decodes them exactly, the product with s * 2^9 is q * s
-// exactly in fp32 and one rounding makes it bf16.  X tiles go to LDS as
-// they are.  v_mfma_f32_32x32x16_bf16 accumulates in fp32.
+// into 32 bf16 weights on their way into LDS: the two units' matrix-core
+// words (code layout) hold the codes as FP6 E2M3 values q/8, which
+// v_cvt_scalef32_pk32_f32_fp6 decodes exactly, in k order; the product with
+// 8 s is q s exactly in fp32 and one rounding makes it bf16.  X tiles go to
+// LDS as they are.  v_mfma_f32_32x32x16_bf16 accumulates in fp32.
 // ---------------------------------------------------------------------------
 constexpr int kW16Row = 64 * 2 + 16;            // LDS row: 64 bf16 + 16 bytes padding
 constexpr int kW16Slot = 2 * kTile * kW16Row;   // W rows, then X rows
@@ -1340,22 +1404,13 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_w4a16(
   };
   auto lstore = [&](auto buf_c, LoadRegs L) {
     constexpr int buf = decltype(buf_c)::value;
-    const float sc = f16_bits_to_f32(L.s) * 512.0f;        // s * 2^9
-    const uint32_t w4[4] = {L.w.x, L.w.y, L.w.z, L.w.w};
+    const float sc = f16_bits_to_f32(L.s) * 8.0f;          // 8 s: (q/8) (8 s) = q s exactly
+    const v6u d = {L.w.x & ~kZ0, L.w.y & ~kZ1, (L.w.x & kZ0) | (L.w.y & kZ1),
+                   L.w.z & ~kZ0, L.w.w & ~kZ1, (L.w.z & kZ0) | (L.w.w & kZ1)};
+    const v32f v = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(d, 1.0f);   // q/8 of the 32 codes, in k order
     uint32_t o[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t E = w4[i] & 0x87878787u;
-      const uint32_t O = __builtin_amdgcn_alignbit(w4[i], w4[i], 4) & 0x87878787u;
-      const v2f e01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(E), false);   // k 8i+0, 8i+2
-      const v2f e23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(E), true);    // k 8i+4, 8i+6
-      const v2f o01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(O), false);   // k 8i+1, 8i+3
-      const v2f o23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(O), true);    // k 8i+5, 8i+7
-      o[4 * i + 0] = cvt_pk_bf16(e01[0] * sc, o01[0] * sc);
-      o[4 * i + 1] = cvt_pk_bf16(e01[1] * sc, o01[1] * sc);
-      o[4 * i + 2] = cvt_pk_bf16(e23[0] * sc, o23[0] * sc);
-      o[4 * i + 3] = cvt_pk_bf16(e23[1] * sc, o23[1] * sc);
-    }
+    for (int i = 0; i < 16; ++i) o[i] = cvt_pk_bf16(v[2 * i] * sc, v[2 * i + 1] * sc);
     uint4* wd = reinterpret_cast<uint4*>(&lds_c[buf][0] + wdst);
     wd[0] = make_uint4(o[0], o[1], o[2], o[3]);
     wd[1] = make_uint4(o[4], o[5], o[6], o[7]);
@@ -1415,8 +1470,8 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_w4a16(
     if (g + 1 < G) iteration(g + 1, Slot<1>{});
   }
 
-  epilogue_tile128<0>(acc, reinterpret_cast<uint16_t*>(&lds_c[0][0]), nullptr, nullptr, bias, y, M, N, 0, n0, m0, wn,
-                      wm, l32, h, tid, MlpOut{});
+  epilogue_tile128<0>(acc, stage_tile(reinterpret_cast<uint16_t*>(&lds_c[0][0])), nullptr, nullptr, bias, y, M, N, 0,
+                      n0, m0, wn, wm, l32, h, tid, MlpOut{});
 }
 
 // K1 grid: 64-row blocks x K slices.  The slice count is chosen so that

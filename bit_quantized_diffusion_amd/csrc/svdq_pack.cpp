@@ -370,6 +370,31 @@ void top_eigs(const double* G, int d, int r, std::vector<double>& U, std::vector
 
 // --------------------------- quantizers ------------------------------------
 
+// Code layout of the INT4 codes: units of 16 consecutive k in two
+// little-endian 32-bit words.  Code q has the 6-bit image 32 [q < 0] + |q|
+// (the FP6 E2M3 pattern of q/8); image j of a unit sits at bits 6j..6j+5 of
+// the 96-bit string D0 | D1 << 32 | D2 << 64, and the unit is stored as
+// I0 = D0 | (D2 & 0x18618618), I1 = D1 | (D2 & 0x86186186): the two masks
+// are the always-zero bits 3-4 of the images in D0 and D1, which together
+// are exactly the data bits of D2.  n codes (n % 16 == 0) -> n / 2 bytes.
+void pack_int4_units(const int* q, int n, uint8_t* out) {
+  for (int u = 0; u < n / 16; ++u) {
+    uint32_t d[3] = {0, 0, 0};
+    for (int j = 0; j < 16; ++j) {
+      const int c = q[16 * u + j];
+      const uint32_t f = c < 0 ? 32u + static_cast<uint32_t>(-c) : static_cast<uint32_t>(c);
+      const int bit = 6 * j, w = bit / 32, o = bit % 32;
+      d[w] |= f << o;
+      if (o + 6 > 32) d[w + 1] |= f >> (32 - o);
+    }
+    const uint32_t i0 = d[0] | (d[2] & 0x18618618u), i1 = d[1] | (d[2] & 0x86186186u);
+    for (int b = 0; b < 4; ++b) {
+      out[8 * u + b] = static_cast<uint8_t>(i0 >> (8 * b));
+      out[8 * u + 4 + b] = static_cast<uint8_t>(i1 >> (8 * b));
+    }
+  }
+}
+
 void quant_int4_row(const float* v, int K, uint8_t* q_packed, uint16_t* scale_bits, int64_t scale_stride) {
   for (int g = 0; g < K / kInt4Group; ++g) {
     const float* gv = v + g * kInt4Group;
@@ -384,21 +409,10 @@ void quant_int4_row(const float* v, int K, uint8_t* q_packed, uint16_t* scale_bi
       continue;
     }
     const float inv = 1.0f / s;
-    // 8 codes per little-endian word: each code as the byte s000_0mmm,
-    // E = the even-k bytes, O = the odd-k bytes, word = E | rotl32(O, 4)
-    for (int i = 0; i < kInt4Group; i += 8) {
-      uint32_t e = 0, o = 0;
-      for (int j = 0; j < 4; ++j) {
-        int q0 = static_cast<int>(std::nearbyint(gv[i + 2 * j] * inv));
-        int q1 = static_cast<int>(std::nearbyint(gv[i + 2 * j + 1] * inv));
-        q0 = std::min(7, std::max(-7, q0));
-        q1 = std::min(7, std::max(-7, q1));
-        e |= static_cast<uint32_t>(q0 < 0 ? (0x80 | -q0) : q0) << (8 * j);
-        o |= static_cast<uint32_t>(q1 < 0 ? (0x80 | -q1) : q1) << (8 * j);
-      }
-      const uint32_t word = e | (o << 4) | (o >> 28);
-      for (int b = 0; b < 4; ++b) out[i / 2 + b] = static_cast<uint8_t>(word >> (8 * b));
-    }
+    int q[kInt4Group];
+    for (int i = 0; i < kInt4Group; ++i)
+      q[i] = std::min(7, std::max(-7, static_cast<int>(std::nearbyint(gv[i] * inv))));
+    pack_int4_units(q, kInt4Group, out);
   }
 }
 

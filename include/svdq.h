@@ -32,13 +32,14 @@
  *    stored the same way: lora_down = L1^T as [rank][K] and lora_up = L2^T
  *    as [N][rank], i.e. the weights of the two small linears K->rank and
  *    rank->N.
- *  - INT4 codes, q in [-7, 7]: 4 bits each, rows of K/2 bytes, 8
- *    consecutive k per little-endian 32-bit word.  Each code taken as the
- *    byte s000_0mmm (bit 7 = sign of a negative code, bits 0-2 = |q|), E =
- *    the word of the 4 even-k bytes (byte j = k 8w+2j), O = that of the 4
- *    odd-k bytes; the stored word is E | rotl32(O, 4).  (So byte j holds
- *    |e_j| in bits 0-2, its sign in bit 7, |o_j| in bits 4-6 and the sign of
- *    o_(j+3)%4 in bit 3; E = w & 0x87878787, O = rotr32(w, 4) & 0x87878787.)
+ *  - INT4 codes, q in [-7, 7]: 4 bits each, rows of K/2 bytes, in units of
+ *    16 consecutive k stored as two little-endian 32-bit words I0, I1.
+ *    Code q has the 6-bit image 32 [q < 0] + |q| (sign in bit 5, |q| in
+ *    bits 0-2, bits 3-4 zero: the FP6 E2M3 pattern of q/8); image j of a
+ *    unit sits at bits 6j..6j+5 of the 96-bit string D0 | D1<<32 | D2<<64,
+ *    and I0 = D0 | (D2 & 0x18618618), I1 = D1 | (D2 & 0x86186186) (the
+ *    masks are the zero bits 3-4 of the images in D0 and D1, which together
+ *    are the data bits of D2).  Zero carries no sign.
  *    INT4 scales: fp16, one per 64 consecutive k of a row, group-major
  *    [K/64][rows].  MXFP4 codes: E2M1 nibbles (sign in bit 3), code k in
  *    the low nibble of byte k/2 when k is even;

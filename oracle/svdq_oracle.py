@@ -36,12 +36,17 @@ both this oracle and the GPU path):
       s = fp16(fp32(amax / 7)) with round-to-nearest-even and saturation at
       65504; s == 0 -> all codes 0; otherwise inv = fp32(1/s) and
       q = clamp(rint(fp32(v * inv)), -7, 7), ties to even.
-  R6  codes take 4 bits each, row-major [rows][K/2], 8 consecutive k per
-      little-endian 32-bit word: with each code as the byte s000_0mmm
-      (sign of a negative code in bit 7, |q| in bits 0-2), E the word of
-      the 4 even-k bytes and O that of the 4 odd-k bytes, the word is
-      E | rotl32(O, 4).  Sign and magnitude hold exactly the symmetric
-      range [-7, 7] of the quantizer.  Scales are group-major [K/64][rows].
+  R6  codes take 4 bits each, row-major [rows][K/2], in units of 16
+      consecutive k stored as two little-endian 32-bit words (I0, I1).  A
+      code q has the 6-bit image f(q) = 32 [q < 0] + |q| (sign in bit 5,
+      |q| in bits 0-2, bits 3-4 zero: the FP6 E2M3 pattern of q/8).  The 16
+      images of a unit, the j-th at bits 6j..6j+5, form a 96-bit string
+      D0 | D1 << 32 | D2 << 64; then I0 = D0 | (D2 & Z0) and
+      I1 = D1 | (D2 & Z1) with Z0 = 0x18618618 and Z1 = 0x86186186 -- the
+      zero bits 3-4 of the images in D0 and D1, which together are exactly
+      the 21 data bits of D2.  Sign and magnitude hold the quantizer's
+      symmetric range [-7, 7]; zero carries no sign.  Scales are
+      group-major [K/64][rows].
   R7  x^ = bf16(fp32(x * smooth_inv)), rounded once and used by both branches.
   R8  down projection t = X^ L1 in fp64 (the GPU keeps it in fp32 [M][r]);
       the up projection uses bf16(fp32(t)).
@@ -131,52 +136,62 @@ def quantize_groups(v):
     return q.reshape(rows, K), s
 
 
-def _code_bytes(q) -> np.ndarray:
-    """int codes in [-7, 7] -> the byte s000_0mmm (bit 7 set for a negative
-    code, bits 0-2 = |q|; zero carries no sign)."""
-    q = np.asarray(q).astype(np.int16)
+_Z0 = 0x18618618     # bits 3,4 9,10 15,16 21,22 27,28: the zero bits 3-4 of the images in D0
+_Z1 = 0x86186186     # bits 1,2 7,8 13,14 19,20 25,26 31: the same in D1
+_UNIT = 16           # codes per unit (two 32-bit words)
+
+
+def _images(q) -> np.ndarray:
+    """int codes in [-7, 7] -> 6-bit images 32 [q < 0] + |q| (zero has no sign)."""
+    q = np.asarray(q).astype(np.int64)
     assert np.all(np.abs(q) <= 7), "4-bit codes hold [-7, 7]"
-    return np.where(q < 0, 0x80 | (-q), q).astype(np.uint32)
+    return np.where(q < 0, 32 - q, q).astype(np.uint64)
 
 
 def pack_int4(q) -> np.ndarray:
-    """int8 codes [rows][K] (K % 8 == 0) in [-7, 7] -> uint8 [rows][K/2]
-    (reading R6).  Each little-endian 32-bit word holds 8 consecutive k.
-    With E the word whose byte j is the code byte of k = 8w + 2j and O the
-    word of the odd k = 8w + 2j + 1, the stored word is E | rotl32(O, 4):
-    byte j keeps |e_j| in bits 0-2 and its sign in bit 7, |o_j| in bits 4-6,
-    and bit 3 carries the sign of o_{(j+3) % 4}."""
-    b = _code_bytes(q)
-    rows, K = b.shape
-    assert K % 8 == 0
-    b = b.reshape(rows, K // 8, 4, 2)
-    E = np.zeros((rows, K // 8), np.uint64)
-    O = np.zeros((rows, K // 8), np.uint64)
-    for j in range(4):
-        E |= b[:, :, j, 0].astype(np.uint64) << np.uint64(8 * j)
-        O |= b[:, :, j, 1].astype(np.uint64) << np.uint64(8 * j)
-    rot = ((O << np.uint64(4)) | (O >> np.uint64(28))) & np.uint64(0xFFFFFFFF)
-    words = (E | rot).astype("<u4")
+    """int codes [rows][K] (K % 16 == 0) in [-7, 7] -> uint8 [rows][K/2]
+    (reading R6): per unit of 16 consecutive k, the images f_j at bits
+    6j..6j+5 of the 96-bit string D0 | D1 << 32 | D2 << 64, stored as
+    I0 = D0 | (D2 & Z0), I1 = D1 | (D2 & Z1)."""
+    f = _images(q)
+    rows, K = f.shape
+    assert K % _UNIT == 0
+    f = f.reshape(rows, K // _UNIT, _UNIT)
+    D = [np.zeros((rows, K // _UNIT), np.uint64) for _ in range(3)]
+    for j in range(_UNIT):
+        bit = 6 * j
+        w, o = bit // 32, bit % 32
+        D[w] |= (f[:, :, j] << np.uint64(o)) & np.uint64(0xFFFFFFFF)
+        if o + 6 > 32:                              # the image straddles two words
+            D[w + 1] |= f[:, :, j] >> np.uint64(32 - o)
+    z0, z1 = np.uint64(_Z0), np.uint64(_Z1)
+    assert not np.any(D[0] & z0) and not np.any(D[1] & z1)
+    assert not np.any(D[2] & ~(z0 | z1) & np.uint64(0xFFFFFFFF))
+    words = np.stack([D[0] | (D[2] & z0), D[1] | (D[2] & z1)], axis=2).astype("<u4")
     return np.ascontiguousarray(words).view(np.uint8).reshape(rows, K // 2)
 
 
 def unpack_int4(p) -> np.ndarray:
-    """Inverse of pack_int4: E = w & 0x87878787, O = rotr32(w, 4) &
-    0x87878787, each byte read as sign (bit 7) and magnitude (bits 0-2)."""
+    """Inverse of pack_int4: D0 = I0 & ~Z0, D1 = I1 & ~Z1,
+    D2 = (I0 & Z0) | (I1 & Z1); image j = bits 6j..6j+5 of the 96-bit
+    string, read as sign (bit 5) and magnitude (bits 0-2)."""
     p = np.ascontiguousarray(p, dtype=np.uint8)
     rows, nb = p.shape
-    assert nb % 4 == 0
-    w = p.view("<u4").astype(np.uint64)
-    mask = np.uint64(0x87878787)
-    E = w & mask
-    O = ((w >> np.uint64(4)) | (w << np.uint64(28))) & mask
-    out = np.empty((rows, nb * 2), dtype=np.int8)
-    for j in range(4):
-        for parity, X in ((0, E), (1, O)):
-            byte = (X >> np.uint64(8 * j)) & np.uint64(0xFF)
-            mag = (byte & np.uint64(7)).astype(np.int8)
-            out[:, 2 * j + parity::8] = np.where(byte & np.uint64(0x80), -mag, mag)
-    return out
+    assert nb % 8 == 0
+    w = p.view("<u4").astype(np.uint64).reshape(rows, nb // 8, 2)
+    z0, z1, m32 = np.uint64(_Z0), np.uint64(_Z1), np.uint64(0xFFFFFFFF)
+    D = [w[:, :, 0] & ~z0 & m32, w[:, :, 1] & ~z1 & m32, (w[:, :, 0] & z0) | (w[:, :, 1] & z1)]
+    out = np.empty((rows, nb // 8, _UNIT), dtype=np.int8)
+    for j in range(_UNIT):
+        bit = 6 * j
+        wd, o = bit // 32, bit % 32
+        f = D[wd] >> np.uint64(o)
+        if o + 6 > 32:
+            f = f | (D[wd + 1] << np.uint64(32 - o))
+        f = f & np.uint64(63)
+        mag = (f & np.uint64(7)).astype(np.int8)
+        out[:, :, j] = np.where(f & np.uint64(32), -mag, mag)
+    return out.reshape(rows, nb * 2)
 
 
 # ---------------------------------------------------------------------------

@@ -195,18 +195,47 @@ def test_quantizer_error_bound():
 
 
 def test_pack_bytes_and_roundtrip():
-    # code bytes: 1 -> 0x01, -1 -> 0x81, -7 -> 0x87, 7 -> 0x07, 0 -> 0x00,
-    # -5 -> 0x85, 3 -> 0x03, -3 -> 0x83.  E (k even) = 0x03008701, O (k odd)
-    # = 0x83850781, rotl32(O, 4) = 0x38507818, E | rotl = 0x3b50ff19, stored
-    # little-endian
-    q = np.array([[1, -1, -7, 7, 0, -5, 3, -3]], dtype=np.int8)
-    p = O.pack_int4(q)
-    assert list(p[0]) == [0x19, 0xFF, 0x50, 0x3B]
+    # Unit [1, -1, -7, 7, 0, -5, 3, -3, 2, -2, 4, -4, 5, 6, -6, 0], worked by
+    # hand: images f = [1, 33, 39, 7, 0, 37, 3, 35, 2, 34, 4, 36, 5, 6, 38, 0].
+    # D0 = 1 + 33<<6 + 39<<12 + 7<<18 + 0<<24 + (37 & 3)<<30 = 0x401e7841;
+    # D1 = 37>>2 + 3<<4 + 35<<10 + 2<<16 + 34<<22 + (4 & 15)<<28 = 0x48828c39;
+    # D2 = 4>>4 + 36<<2 + 5<<8 + 6<<14 + 38<<20 + 0<<26 = 0x02618590.
+    # I0 = D0 | (D2 & 0x18618618) = 0x401e7841 | 0x00618410 = 0x407ffc51,
+    # I1 = D1 | (D2 & 0x86186186) = 0x48828c39 | 0x02000180 = 0x4a828db9.
+    q = np.array([[1, -1, -7, 7, 0, -5, 3, -3, 2, -2, 4, -4, 5, 6, -6, 0]], dtype=np.int8)
+    assert list(O.pack_int4(q)[0]) == [0x51, 0xFC, 0x7F, 0x40, 0xB9, 0x8D, 0x82, 0x4A]
+    # all +7: D0 = 0xc71c71c7, D1 = 0x71c71c71, D2 = 0x1c71c71c -> I0 = 0xdf7df7df, I1 = 0x75d75d75
+    assert list(O.pack_int4(np.full((1, 16), 7, np.int8))[0]) == [0xDF, 0xF7, 0x7D, 0xDF, 0x75, 0x5D, 0xD7, 0x75]
     rng = np.random.default_rng(1)
     q = rng.integers(-7, 8, (9, 128)).astype(np.int8)
     assert np.array_equal(O.unpack_int4(O.pack_int4(q)), q)
-    # sign bits on zero magnitudes decode to 0
-    assert O.unpack_int4(np.array([[0x88, 0x88, 0x88, 0x88]], np.uint8)).tolist() == [[0] * 8]
+    # a sign bit on a zero magnitude decodes to 0
+    d2 = 0x20 << 2                                   # image 11 = 0x20 (-0) at bits 2..7 of D2
+    z1 = d2 & 0x86186186                             # its sign bit 7 lies in Z1
+    w = np.array([[0, 0, 0, 0] + list(int(z1).to_bytes(4, "little"))], np.uint8)
+    assert O.unpack_int4(w).tolist() == [[0] * 16]
+
+
+def test_packed_unit_reads_as_fp6_e2m3():
+    """The unit's three words D0, D1, D2, recovered from I0, I1 with the
+    masks, hold the codes as FP6 E2M3 values q/8 (sign bit 5, exponent
+    bits 3-4, mantissa bits 0-2; exponent 0 = subnormal m/8), the j-th at
+    bits 6j of the 96-bit string: decoded by the E2M3 definition, not by
+    unpack_int4."""
+    rng = np.random.default_rng(2)
+    q = rng.integers(-7, 8, (5, 64)).astype(np.int8)
+    p = O.pack_int4(q).view("<u4").reshape(5, 4, 2).astype(np.uint64)
+    for r in range(5):
+        for u in range(4):
+            i0, i1 = int(p[r, u, 0]), int(p[r, u, 1])
+            d = (i0 & ~0x18618618 & 0xFFFFFFFF) | ((i1 & ~0x86186186 & 0xFFFFFFFF) << 32) | \
+                (((i0 & 0x18618618) | (i1 & 0x86186186)) << 64)
+            for j in range(16):
+                f = (d >> (6 * j)) & 63
+                sign, e, m = f >> 5, (f >> 3) & 3, f & 7
+                val = (m / 8.0) if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 1)
+                assert e == 0
+                assert (-val if sign else val) == q[r, 16 * u + j] / 8.0
 
 
 # ---------------------------------------------------------------------------
