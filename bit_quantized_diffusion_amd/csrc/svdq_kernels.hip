@@ -614,6 +614,66 @@ __device__ __forceinline__ void mlp_tail(const StageTile& stg, int M, int N, int
   }
 }
 
+// acc += bf16(lora_act) . L2 (16 ranks per v_mfma_f32_32x32x16_bf16) on the
+// accumulators of a 128 x 128 tile (4 waves of 64 x 64, Y^T MFMA layout).
+__device__ __forceinline__ void lora_up_acc(v16f (&acc)[2][2], const float* __restrict__ lact,
+                                            const uint16_t* __restrict__ lup, int M, int N, int rank, int n0, int m0,
+                                            int wn, int wm, int l32, int h) {
+  for (int c0 = 0; c0 < rank; c0 += 16) {
+    const int j = c0 + 8 * h;
+    v4i ub[2], ua[2];
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+      const int m = m0 + wm * 64 + jt * 32 + l32;
+      ub[jt] = v4i{0, 0, 0, 0};
+      if (m < M) {
+        const float4* src = reinterpret_cast<const float4*>(lact + static_cast<size_t>(m) * rank + j);
+        const float4 f0 = src[0], f1 = src[1];
+        ub[jt] = v4i{static_cast<int>(pack_bf16_rne(f0.x, f0.y)), static_cast<int>(pack_bf16_rne(f0.z, f0.w)),
+                     static_cast<int>(pack_bf16_rne(f1.x, f1.y)), static_cast<int>(pack_bf16_rne(f1.z, f1.w))};
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int n = n0 + wn * 64 + it * 32 + l32;
+      ua[it] = n < N ? *reinterpret_cast<const v4i*>(lup + static_cast<size_t>(n) * rank + j) : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+        acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ua[it]),
+                                                              __builtin_bit_cast(v8bf, ub[jt]), acc[it][jt], 0, 0, 0);
+  }
+}
+
+// The tile's bias values: lane element 4j+i of tile it is channel
+// n0 + wn*64 + it*32 + 8j + 4h + i (zero without a bias).
+__device__ __forceinline__ void load_bias(float (&bv)[2][4][4], const uint16_t* __restrict__ bias, int N, int n0, int wn,
+                                          int h) {
+#pragma unroll
+  for (int it = 0; it < 2; ++it)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int nb = n0 + wn * 64 + it * 32 + 8 * j + 4 * h;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bv[it][j][i] = 0.f;
+      if (bias) {
+        if ((N % 4) == 0 && nb + 3 < N) {
+          const uint2 b2 = *reinterpret_cast<const uint2*>(bias + nb);
+          bv[it][j][0] = __uint_as_float(b2.x << 16);
+          bv[it][j][1] = __uint_as_float(b2.x & 0xFFFF0000u);
+          bv[it][j][2] = __uint_as_float(b2.y << 16);
+          bv[it][j][3] = __uint_as_float(b2.y & 0xFFFF0000u);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (nb + i < N) bv[it][j][i] = __uint_as_float(static_cast<uint32_t>(bias[nb + i]) << 16);
+        }
+      }
+    }
+}
+
 // Shared epilogue of the 128 x 128 GEMM tiles (4 waves of 64 x 64, Y^T
 // MFMA layout): acc += bf16(lora_act) . L2 on the accumulators (16 ranks per
 // v_mfma_f32_32x32x16_bf16), the bias, one rounding to bf16, then the tile
@@ -632,7 +692,9 @@ __device__ __forceinline__ void mlp_tail(const StageTile& stg, int M, int N, int
 // 16-byte chunk c of row r at chunk c ^ (r % 8)) and L2 rows (128 x 32 bf16
 // at byte 16384, 64-byte rows, chunk c of row r at c ^ ((r / 4) % 4)) are
 // already in LDS at upl.
-template <int EPI, bool UPL = false>
+// PRE: the low-rank term and the bias are already in acc (lora_up_acc and
+// load_bias at the start of the tile).
+template <int EPI, bool UPL = false, bool PRE = false>
 __device__ __forceinline__ void epilogue_tile128(v16f (&acc)[2][2], const StageTile& stg,
                                                  const float* __restrict__ lact, const uint16_t* __restrict__ lup,
                                                  const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M,
@@ -666,56 +728,10 @@ __device__ __forceinline__ void epilogue_tile128(v16f (&acc)[2][2], const StageT
                                                                 __builtin_bit_cast(v8bf, ub[jt]), acc[it][jt], 0, 0, 0);
     }
   }
-  for (int c0 = 0; c0 < (UPL ? 0 : rank); c0 += 16) {
-    const int j = c0 + 8 * h;
-    v4i ub[2], ua[2];
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt) {
-      const int m = m0 + wm * 64 + jt * 32 + l32;
-      ub[jt] = v4i{0, 0, 0, 0};
-      if (m < M) {
-        const float4* src = reinterpret_cast<const float4*>(lact + static_cast<size_t>(m) * rank + j);
-        const float4 f0 = src[0], f1 = src[1];
-        ub[jt] = v4i{static_cast<int>(pack_bf16_rne(f0.x, f0.y)), static_cast<int>(pack_bf16_rne(f0.z, f0.w)),
-                     static_cast<int>(pack_bf16_rne(f1.x, f1.y)), static_cast<int>(pack_bf16_rne(f1.z, f1.w))};
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int n = n0 + wn * 64 + it * 32 + l32;
-      ua[it] = n < N ? *reinterpret_cast<const v4i*>(lup + static_cast<size_t>(n) * rank + j) : v4i{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int it = 0; it < 2; ++it)
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
-        acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ua[it]),
-                                                              __builtin_bit_cast(v8bf, ub[jt]), acc[it][jt], 0, 0, 0);
-  }
+  if constexpr (!PRE) lora_up_acc(acc, lact, lup, M, N, UPL ? 0 : rank, n0, m0, wn, wm, l32, h);
 
-  // bias: lane element 4j+i of tile it is channel n0 + wn*64 + it*32 + 8j + 4h + i
   float bv[2][4][4];
-#pragma unroll
-  for (int it = 0; it < 2; ++it)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int nb = n0 + wn * 64 + it * 32 + 8 * j + 4 * h;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bv[it][j][i] = 0.f;
-      if (bias) {
-        if ((N % 4) == 0 && nb + 3 < N) {
-          const uint2 b2 = *reinterpret_cast<const uint2*>(bias + nb);
-          bv[it][j][0] = __uint_as_float(b2.x << 16);
-          bv[it][j][1] = __uint_as_float(b2.x & 0xFFFF0000u);
-          bv[it][j][2] = __uint_as_float(b2.y << 16);
-          bv[it][j][3] = __uint_as_float(b2.y & 0xFFFF0000u);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (nb + i < N) bv[it][j][i] = __uint_as_float(static_cast<uint32_t>(bias[nb + i]) << 16);
-        }
-      }
-    }
+  load_bias(bv, PRE ? nullptr : bias, N, n0, wn, h);
 
   // Y = bf16(acc + bias), one rounding, into the staging tile [m][n]
 #pragma unroll
@@ -1011,6 +1027,39 @@ __device__ __forceinline__ v8i fp6_words(const uint4& w) {
              0, 0};
 }
 
+// LDS address of a __shared__ object: the low 32 bits of its flat address.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)p));
+}
+
+// buffer_load ... lds written as inline asm, so that the compiler neither
+// counts these loads nor waits for them: a kernel that issues them orders
+// them itself with s_waitcnt vmcnt and barriers (lds_wait_barrier).  M0
+// holds the LDS address (one wait state between its write and the load).
+// 16 bytes per lane land at M0 + 16 lane; 2 bytes per lane land,
+// zero-extended, in the 4-byte slot M0 + 4 lane.
+__device__ __forceinline__ void dma_b128(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff, int soff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(r), "s"(soff), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+__device__ __forceinline__ void dma_u16(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff, int soff) {
+  asm volatile("s_nop 0\n\tbuffer_load_ushort %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(r), "s"(soff), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+// wait until at most N of the wave's vector-memory loads are outstanding
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+// the wave's LDS accesses done and at most N loads outstanding, then the
+// workgroup barrier
+template <int N>
+__device__ __forceinline__ void lds_wait_barrier() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
 template <bool DEBUG, int EPI = 0>
 __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
     const uint8_t* __restrict__ xq, const uint16_t* __restrict__ xs,
@@ -1026,16 +1075,12 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   __shared__ __attribute__((aligned(16))) uint8_t x_ring2[kI4Op];
   auto wring = [&](int slot) __attribute__((always_inline)) { return slot == 0 ? w_ring0 : slot == 1 ? w_ring1 : w_ring2; };
   auto xring = [&](int slot) __attribute__((always_inline)) { return slot == 0 ? x_ring0 : slot == 1 ? x_ring1 : x_ring2; };
-  // per slot, operand and row: the scale words of the stage's two groups
-  // {g0 word0, g0 word1, g1 word0, g1 word1} (sstore)
-  __shared__ __attribute__((aligned(16))) uint4 ws_ring0[kTile];
-  __shared__ __attribute__((aligned(16))) uint4 xs_ring0[kTile];
-  __shared__ __attribute__((aligned(16))) uint4 ws_ring1[kTile];
-  __shared__ __attribute__((aligned(16))) uint4 xs_ring1[kTile];
-  __shared__ __attribute__((aligned(16))) uint4 ws_ring2[kTile];
-  __shared__ __attribute__((aligned(16))) uint4 xs_ring2[kTile];
-  auto wsring = [&](int slot) __attribute__((always_inline)) { return slot == 0 ? ws_ring0 : slot == 1 ? ws_ring1 : ws_ring2; };
-  auto xsring = [&](int slot) __attribute__((always_inline)) { return slot == 0 ? xs_ring0 : slot == 1 ? xs_ring1 : xs_ring2; };
+  // raw fp16 scales as loaded, [slot][operand W, X][group][row], one per
+  // 4-byte slot; two slots (stage st lands in slot st % 2)
+  __shared__ __attribute__((aligned(16))) uint32_t s_raw[2][2][2][kTile];
+  // split scale words, [slot][operand W, X][row]: {g0 word0, g0 word1,
+  // g1 word0, g1 word1} (split); stage st's in slot st % 2
+  __shared__ __attribute__((aligned(16))) uint4 s_words[2][2][kTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1058,17 +1103,19 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
     m0 = tc.m0;
   }
 
-  // Code loads: waves 0, 1 load W rows, waves 2, 3 X rows, through a
-  // buffer resource based at the tile's first row.  Load j (0..3) of a wave
-  // fills rows 64 (wave % 2) + 16 j .. +15 of its operand: lane i writes LDS
-  // chunk i % 4 of row i / 4 and reads global chunk (i % 4) ^ swz4(row) of
-  // that row; rows past the matrix edge are clamped to its last row, and the
-  // resource bounds every access (a missing second group of an odd-G last
-  // stage reads zeros or the next row, never used).
-  const bool ld_w = wave < 2;                  // wave-uniform
-  const int ld_rows = ld_w ? N - n0 : M - m0;
+  // Loads: waves 0, 1 load W rows, waves 2, 3 X rows; wave w owns rows
+  // 64 (w % 2) .. +63 of its operand.  Per stage a wave issues six loads,
+  // in this order: its rows' fp16 scales of the stage's two groups (lane i
+  // -> row 64 (w % 2) + i), then four code loads, load j filling rows
+  // 64 (w % 2) + 16 j .. +15: lane i writes LDS chunk i % 4 of row i / 4 and
+  // reads global chunk (i % 4) ^ swz4(row) of that row.  Rows past the
+  // matrix edge are clamped to its last row; the resources bound every
+  // access (a missing second group of an odd-G last stage reads zeros or
+  // the next row, never used).
+  const int op = wave >> 1;                    // wave-uniform: 0 W, 1 X
+  const int ld_rows = op == 0 ? N - n0 : M - m0;
   const __amdgpu_buffer_rsrc_t rc =
-      make_rsrc(ld_w ? wq + static_cast<size_t>(n0) * kb : xq + static_cast<size_t>(m0) * kb,
+      make_rsrc(op == 0 ? wq + static_cast<size_t>(n0) * kb : xq + static_cast<size_t>(m0) * kb,
                 static_cast<size_t>(ld_rows) * static_cast<size_t>(kb));
   int vcode[4];
 #pragma unroll
@@ -1076,37 +1123,20 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
     const int r = 64 * (wave & 1) + 16 * j + (lane >> 2);
     vcode[j] = min(r, ld_rows - 1) * kb + (((lane & 3) ^ swz4(r)) << 4);
   }
-  auto dma = [&](int st, int slot) __attribute__((always_inline)) {
-    const int so = st * kI4RowB;
-    if (ld_w) {
-      uint8_t* base = wring(slot) + 64 * (wave & 1) * kI4RowB;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr_t)(base + 16 * j * kI4RowB), 16, vcode[j], so, 0, 0);
-    } else {
-      uint8_t* base = xring(slot) + 64 * (wave & 1) * kI4RowB;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr_t)(base + 16 * j * kI4RowB), 16, vcode[j], so, 0, 0);
-    }
-  };
-  // Scales: thread t < 128 reads W row n0 + t, t >= 128 X row m0 + t - 128
-  // (clamped into the matrix), both groups of a stage.
-  const bool s_is_w = wave < 2;                // wave-uniform
-  const int s_row = tid & (kTile - 1);
-  const int s_rows = s_is_w ? N : M;
+  const int s_rows = op == 0 ? N : M;
+  const int s_row = tid & (kTile - 1);         // = 64 (wave % 2) + lane
+  const int gbytes = 2 * s_rows;               // bytes per group of the scale array
   const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(s_is_w ? ws : xs, static_cast<size_t>(G) * static_cast<size_t>(s_rows) * 2);
-  const int vs = 2 * min((s_is_w ? n0 : m0) + s_row, s_rows - 1);
-  const int gstride = 2 * s_rows;              // bytes per group of the scale array
-  auto sload = [&](int st) __attribute__((always_inline)) {
-    uint2 s = make_uint2(0u, 0u);
-    if constexpr (!DEBUG) {
-      const int sso = 2 * st * gstride;
-      s.x = __builtin_amdgcn_raw_buffer_load_b16(rs, vs, sso, 0);
-      if (2 * st + 1 < G) s.y = __builtin_amdgcn_raw_buffer_load_b16(rs, vs + gstride, sso, 0);
-    }
-    return s;
+      make_rsrc(op == 0 ? ws : xs, DEBUG ? 0 : static_cast<size_t>(G) * static_cast<size_t>(gbytes));
+  const int vs = 2 * min((op == 0 ? n0 : m0) + s_row, s_rows - 1);
+  auto dma = [&](int st, auto slot_c) __attribute__((always_inline)) {
+    constexpr int slot = decltype(slot_c)::value;
+    const int sso = 2 * st * gbytes;
+    dma_u16(rs, lds_addr(&s_raw[st & 1][op][0][64 * (wave & 1)]), vs, sso);
+    dma_u16(rs, lds_addr(&s_raw[st & 1][op][1][64 * (wave & 1)]), vs, sso + gbytes);
+    const uint8_t* base = (op == 0 ? wring(slot) : xring(slot)) + 64 * (wave & 1) * kI4RowB;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma_b128(rc, lds_addr(base + 16 * j * kI4RowB), vcode[j], st * kI4RowB);
   };
   // A scale s (fp16 >= 0) splits as s = m 2^e with m in [0.5, 1)
   // (v_frexp_mant_f16, v_frexp_exp_i16_f16, subnormals included; s == 0
@@ -1116,23 +1146,21 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   // Byte 2 of W's word0 and of X's word1 is the E8M0 scale of the FP6 MFMA
   // (op_sel 2); as f16 operands of the rank-1 MFMA ({word0, word1} = k 0-3,
   // the same in k 4-7) W gives [m_w, e_w, 0, 0] and X [m_x, 0, 0, e_x], so
-  // only k 0 and k 4 contribute: 2 m_w m_x, exactly.
-  auto sstore = [&](int slot, const uint2& s) __attribute__((always_inline)) {
+  // only k 0 and k 4 contribute: 2 m_w m_x, exactly.  Thread t splits the
+  // row its own wave loaded (s_row of operand op).
+  auto split = [&](int st) __attribute__((always_inline)) {
     if constexpr (DEBUG) return;
+    const uint32_t raw[2] = {s_raw[st & 1][op][0][s_row], s_raw[st & 1][op][1][s_row]};
     uint32_t wv[4];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const _Float16 sv = __builtin_bit_cast(_Float16, static_cast<uint16_t>(i ? s.y : s.x));
+      const _Float16 sv = __builtin_bit_cast(_Float16, static_cast<uint16_t>(raw[i]));
       const uint32_t m = __builtin_bit_cast(uint16_t, __builtin_amdgcn_frexp_manth(sv));
-      const uint32_t e =
-          static_cast<uint32_t>(__builtin_amdgcn_frexp_exph(sv) + (s_is_w ? 127 + 6 : 127 - 1)) & 0xFFu;
-      wv[2 * i] = s_is_w ? (m | (e << 16)) : m;
-      wv[2 * i + 1] = s_is_w ? 0u : (e << 16);
+      const uint32_t e = static_cast<uint32_t>(__builtin_amdgcn_frexp_exph(sv) + (op == 0 ? 127 + 6 : 127 - 1)) & 0xFFu;
+      wv[2 * i] = op == 0 ? (m | (e << 16)) : m;
+      wv[2 * i + 1] = op == 0 ? 0u : (e << 16);
     }
-    if (s_is_w)
-      wsring(slot)[s_row] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-    else
-      xsring(slot)[s_row] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    s_words[st & 1][op][s_row] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
   };
 
   v16f acc[2][2];
@@ -1175,12 +1203,12 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   struct Scl {
     uint4 w0, w1, x0, x1;
   };
-  auto load_scl = [&](int slot) __attribute__((always_inline)) {
+  auto load_scl = [&](int wslot) __attribute__((always_inline)) {
     Scl c;
-    c.w0 = wsring(slot)[wn * 64 + l32];
-    c.w1 = wsring(slot)[wn * 64 + 32 + l32];
-    c.x0 = xsring(slot)[wm * 64 + l32];
-    c.x1 = xsring(slot)[wm * 64 + 32 + l32];
+    c.w0 = s_words[wslot][0][wn * 64 + l32];
+    c.w1 = s_words[wslot][0][wn * 64 + 32 + l32];
+    c.x0 = s_words[wslot][1][wm * 64 + l32];
+    c.x1 = s_words[wslot][1][wm * 64 + 32 + l32];
     return c;
   };
   // tile-group t = 2 it + jt of group g: the partial P of W tile it and X
@@ -1222,16 +1250,17 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   // over its tile-groups: both MFMAs of tile-group t+1 (the FP6 product and
   // the scale outer product) are issued before the dequant of tile-group t,
   // so the FMAs find their operands done; the second group's chunks are read
-  // and converted while the first group computes.  The stage's last two
-  // tile-groups leave compute with their MFMAs in flight; their dequant
-  // (finish) runs after the stage barrier.
+  // and converted while the first group computes.  The stage's last two tile-groups
+  // leave compute with their MFMAs in flight; their dequant (finish) runs
+  // after the stage barrier.
   v16f pa, pb, ca, cb;
   auto finish = [&]() __attribute__((always_inline)) {
     dqc(I2{}, pa, ca);
     dqc(I3{}, pb, cb);
   };
-  auto compute = [&](int slot, bool one, int g0) __attribute__((always_inline)) {
+  auto compute = [&](int slot, int wslot, bool one, int g0, auto&& pre) __attribute__((always_inline)) {
     if constexpr (DEBUG) {
+      pre();
       auto group = [&](auto g_c) __attribute__((always_inline)) {
         constexpr int g = decltype(g_c)::value;
         const Ops o = cvt(load_raw(slot, g_c));
@@ -1261,7 +1290,8 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
       if (!one) group(I1{});
     } else {
       const Raw r0 = load_raw(slot, I0{});
-      const Scl c = load_scl(slot);
+      const Scl c = load_scl(wslot);
+      pre();
       const Ops o0 = cvt(r0);
       pa = mf(o0, c, I0{}, I0{});
       ca = rk(c, I0{}, I0{});
@@ -1290,43 +1320,57 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
     }
   };
 
-  // prologue: stages 0 and 1 in flight; stage 0 (codes and scales) in LDS
-  {
-    const uint2 s0 = sload(0);
-    dma(0, 0);
-    if (S > 1) {
-      const uint2 s1 = sload(1);
-      dma(1, 1);
-      sstore(0, s0);
-      sstore(1, s1);
-    } else {
-      sstore(0, s0);
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
-    __syncthreads();
+  // Pipeline: at the top of iteration st, stage st (codes and scale words)
+  // is in LDS for every wave and stage st+1's six loads per wave may still
+  // be out.  The iteration reads stage st's first group and scale words,
+  // issues stage st+2's loads (when there is one), finishes stage st-1 and
+  // computes stage st; then, once the wave's own scale loads of stage st+1
+  // have landed (at most the four code loads of stage st+1 and the six of
+  // stage st+2 still out), it splits stage st+1's scales, and it ends with
+  // stage st+1 complete (at most stage st+2's six loads out) and the
+  // barrier.
+  // Prologue: stages 0 and 1 in flight; meanwhile the tile's low-rank term
+  // and bias go into the accumulators (the main loop adds the 4-bit
+  // products to them); then stage 0 complete and split.
+  dma(0, Slot<0>{});
+  if (S > 1) dma(1, Slot<1>{});
+  if constexpr (!DEBUG) {
+    lora_up_acc(acc, lact, lup, M, N, rank, n0, m0, wn, wm, l32, h);
+    float bv[2][4][4];
+    load_bias(bv, bias, N, n0, wn, h);
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[it][jt][r] += bv[it][r / 4][r % 4];
   }
-  // the ring slot of each stage is a compile-time constant (loop unrolled by
-  // three), so that the compiler can tell the stage's LDS reads from the
-  // loads landing in the slot two stages ahead and waits for neither
+  if (S > 1)
+    vm_wait<6>();
+  else
+    vm_wait<0>();
+  split(0);
+  lds_wait_barrier<6>();                       // stage 1's loads may stay out
   auto iteration = [&](int st, auto slot_c) __attribute__((always_inline)) {
     constexpr int slot = decltype(slot_c)::value;
     constexpr int slot2 = (slot + 2) % kI4Slots;
     const bool ahead = st + 2 < S;             // uniform
-    uint2 sn = make_uint2(0u, 0u);
-    if (ahead) {
-      sn = sload(st + 2);
-      dma(st + 2, slot2);
+    compute(slot, st & 1, 2 * st + 1 >= G, 2 * st, [&]() __attribute__((always_inline)) {
+      if (ahead) dma(st + 2, Slot<slot2>{});
+      if constexpr (!DEBUG)
+        if (st > 0) finish();
+    });
+    if (st + 1 < S) {
+      if (ahead)
+        vm_wait<10>();
+      else
+        vm_wait<4>();
+      split(st + 1);
     }
-    if constexpr (!DEBUG)
-      if (st > 0) finish();
-    compute(slot, 2 * st + 1 >= G, 2 * st);
-    if (ahead) {
-      sstore(slot2, sn);
-      __builtin_amdgcn_s_waitcnt(0x0F74);      // vmcnt(4): only this stage's 4 code loads (stage st+2) may be out
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0)
-    }
-    __syncthreads();
+    if (ahead)
+      lds_wait_barrier<6>();
+    else
+      lds_wait_barrier<0>();
   };
   for (int st = 0; st < S; st += 3) {
     iteration(st, Slot<0>{});
@@ -1336,7 +1380,7 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
 
   if constexpr (!DEBUG) finish();
   if constexpr (!DEBUG)
-    epilogue_tile128<EPI>(acc, StageTile{reinterpret_cast<uint16_t*>(w_ring0), reinterpret_cast<uint16_t*>(x_ring0)}, lact,
+    epilogue_tile128<EPI, false, true>(acc, StageTile{reinterpret_cast<uint16_t*>(w_ring0), reinterpret_cast<uint16_t*>(x_ring0)}, lact,
                           lup, bias, y, M, N, rank, n0, m0, wn, wm, l32, h, tid, mo);
 }
 
