@@ -12,6 +12,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <functional>
@@ -310,7 +311,8 @@ void jacobi_eig(std::vector<double>& H, int n, std::vector<double>& evals, std::
 }
 
 // Top-r eigenpairs of the d x d symmetric PSD matrix G.  Returns r eigen
-// vectors as rows of U ([r][d]) and their eigenvalues.
+// vectors as rows of U ([r][d]) and their eigenvalues.  With the environment
+// variable SVDQ_PACK_STATS=1 the iteration count goes to stderr.
 void top_eigs(const double* G, int d, int r, std::vector<double>& U, std::vector<double>& evals) {
   const int b = std::min(d, r + std::max(16, r / 2));
   std::mt19937_64 rng(0x5D0C7E11u);
@@ -335,6 +337,8 @@ void top_eigs(const double* G, int d, int r, std::vector<double>& U, std::vector
     const bool done = it >= 8 && std::fabs(captured - prev) <= 1e-13 * std::max(captured, 1e-300);
     prev = captured;
     if (done || it == 2999) {
+      if (const char* e = std::getenv("SVDQ_PACK_STATS"); e && e[0] == '1')
+        std::fprintf(stderr, "svdq_pack: Gram order %d, rank %d, block %d, %d subspace iterations\n", d, r, b, it + 1);
       // Ritz vectors of the current basis: U = S^T Q (rows)
       U.assign(static_cast<size_t>(r) * d, 0.0);
       for (int c = 0; c < r; ++c) {

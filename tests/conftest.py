@@ -22,6 +22,11 @@ def _gpu_present() -> bool:
 
 
 def pytest_collection_modifyitems(config, items):
+    if os.environ.get("SVDQ_RUN_SLOW") != "1":
+        skip_slow = pytest.mark.skip(reason="slow case: set SVDQ_RUN_SLOW=1")
+        for item in items:
+            if "slow" in item.keywords:
+                item.add_marker(skip_slow)
     if _gpu_present():
         return
     skip = pytest.mark.skip(reason="no GPU in this process")

@@ -158,3 +158,32 @@ def test_merge_lora_rejects_bad_arguments():
     assert e.value.status == bq.SVDQ_ERR_SHAPE
     st = bq.lib.svdq_merge_lora(None, None, 0, None, None, None, 16, K, N, None, None)
     assert st == bq.SVDQ_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
+# The library's pack at the FLUX MLP sizes (slow: about a minute of CPU per
+# case; run with SVDQ_RUN_SLOW=1).  X only supplies the per-channel absmax,
+# so a few hundred rows of the layer's distribution stand in for it (fc2's
+# own X would be fc1's GELU output).  The singular values are those of the
+# bf16 factors: each factor is rounded to bf16 (relative 2^-9 per element),
+# which moves a singular value of the product by up to about 2 * 2^-9 of it
+# -- the oracle's own bf16 factors sit 2.2e-3 off the exact values at fc1 --
+# so against the exact SVD the bound is 2^-8, and against the oracle's bf16
+# factors (the same roundings of nearly the same subspace) 1e-4.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["fc1", "fc2"])
+def test_pack_flux_mlp_size(name):
+    spec = synth.layer_spec(name, M=256, x_from_prev=False)
+    lay, ax = _layer(spec)
+    ref = O.pack_weights(lay["w"], ax, spec.rank)
+    got = bq.pack_weights(lay["w"], ax, spec.rank, want_residual=True)
+    _check_low_rank(spec, lay, ax, got, ref, tol_sig=2.0 ** -8)
+    r = spec.rank
+    low_lib = O.bf16_bits_to_f32(got["lora_down"]).astype(np.float64).T @ \
+        O.bf16_bits_to_f32(got["lora_up"]).astype(np.float64).T
+    low_ref = O.bf16_bits_to_f32(ref["l1"]).astype(np.float64) @ O.bf16_bits_to_f32(ref["l2"]).astype(np.float64)
+    s_lib = np.linalg.svd(low_lib, compute_uv=False)[:r]
+    s_ref = np.linalg.svd(low_ref, compute_uv=False)[:r]
+    assert np.allclose(s_lib, s_ref, rtol=1e-4)
