@@ -76,6 +76,8 @@ def parse():
                    help="skip the fused-vs-unfused (four kernel) comparison")
     p.add_argument("--no-mxfp4", action="store_true", help="skip the MXFP4 timing of the same layers")
     p.add_argument("--no-mlp", action="store_true", help="skip the fused-MLP timing")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the per-config layer timings (QKV, fc1 r48, tiny, M=576 shares)")
     p.add_argument("--no-w4a16", action="store_true",
                    help="skip the W4A16 (4-bit weight, bf16 activation) comparison timing")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -273,6 +275,10 @@ def main():
         w16 = w4a16_layers(bq, torch, np, dev, (s1, s2), (lay1["w"], w2), (lay1["bias"], synth.gen_bias(s2)),
                            (x1, x2), args.sets, stream, per, reps=20)
 
+    configs = None
+    if not args.no_configs:
+        configs = config_lines(bq, torch, np, dev, synth, stream, pk1, lay1, (L1, x1), (L2, x2))
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(lay1, pk1, s1, args.cpu_seconds, args.cpu_chunk)
@@ -292,6 +298,7 @@ def main():
         "mxfp4": mx,
         "mlp_fusion": mlp,
         "w4a16": w16,
+        "configs": configs,
         "offline_pack_s": pack_s,
     }
     print(json.dumps(out), flush=True)
@@ -526,6 +533,130 @@ def mfma_ceiling(bq, torch, stream, precision, reps=3):
     return res
 
 
+def time_layer(bq, torch, np, stream, L, xs_list, M, reps):
+    """Mean K1 and K2 times (HIP events on the library's stream) of the INT4
+    layer L over `reps` calls rotating through the inputs xs_list."""
+    dev = xs_list[0].device
+    G = L.K // 64
+    bufs = [dict(x=x, xq=torch.empty((M, L.K // 2), dtype=torch.uint8, device=dev),
+                 xs=torch.empty((G, M), dtype=torch.float16, device=dev),
+                 la=torch.empty((M, L.rank), dtype=torch.float32, device=dev),
+                 y=torch.empty((M, L.N), dtype=torch.bfloat16, device=dev)) for x in xs_list]
+
+    def call(b):
+        bq.quantize_act_lora_down(b["x"], L.smooth_inv, L.lora_down, L.rank, xq=b["xq"], xs=b["xs"], lora_act=b["la"])
+        bq.gemm_w4a4_lora_up(b["xq"], b["xs"], L.wq, L.ws, b["la"], L.lora_up, L.bias, M, L.N, L.K, L.rank, y=b["y"])
+
+    for i in range(3):
+        call(bufs[i % len(bufs)])
+    torch.cuda.synchronize()
+    evs = []
+    for i in range(reps):
+        b = bufs[i % len(bufs)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        bq.quantize_act_lora_down(b["x"], L.smooth_inv, L.lora_down, L.rank, xq=b["xq"], xs=b["xs"], lora_act=b["la"])
+        e[1].record(stream)
+        bq.gemm_w4a4_lora_up(b["xq"], b["xs"], L.wq, L.ws, b["la"], L.lora_up, L.bias, M, L.N, L.K, L.rank, y=b["y"])
+        e[2].record(stream)
+        evs.append(e)
+    torch.cuda.synchronize()
+    k1 = [1e3 * e[0].elapsed_time(e[1]) for e in evs]
+    k2 = [1e3 * e[1].elapsed_time(e[2]) for e in evs]
+    lay = [a + b for a, b in zip(k1, k2)]
+    ops = 2.0 * M * L.N * L.K
+    us = float(np.mean(lay))
+    return {"M": M, "K": L.K, "N": L.N, "rank": L.rank, "us_k1": round(float(np.mean(k1)), 2),
+            "us_k2": round(float(np.mean(k2)), 2), "us_layer": round(us, 2),
+            "us_layer_median": round(float(np.median(lay)), 2),
+            "tops": round(ops / (us * 1e-6) / 1e12, 1),
+            "pct_int8_roofline": round(100 * ops / (us * 1e-6) / 1e12 / INT8_PEAK_TOPS, 2)}
+
+
+def config_lines(bq, torch, np, dev, synth, stream, pk1, lay1, fc1, fc2):
+    """The other configurations one GPU can show, timed outside the step:
+    the fused QKV projection (4608x3072->9216, rank 32), fc1 with a rank-16
+    LoRA merged into its branch (rank 48), the tiny case (256x512->512, rank
+    16; launch-bound, so median of the calls), and fc1 / fc2 at M = 576 (the
+    token rows one of eight GPUs holds when the 4608 rows are split)."""
+    out = {}
+
+    def to_dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # C1: fused QKV
+    sq = synth.layer_spec("qkv")
+    lq = synth.gen_layer(sq)
+    xq_ = to_dev_bf16(lq["x"])
+    axq = xq_.float().abs().amax(dim=0).cpu().numpy().astype(np.float32)
+    Lq = bq.PackedLinear.from_host(bq.pack_weights(lq["w"], axq, sq.rank), lq["bias"], sq.rank, device=dev)
+    out["qkv"] = time_layer(bq, torch, np, stream, Lq, [xq_, xq_.clone()], sq.M, reps=20)
+    del Lq, xq_
+    # C3: fc1 + rank-16 LoRA merged (rank 48)
+    sl = synth.layer_spec("fc1_lora")
+    a_bits, b_bits = synth.gen_lora(sl)
+    down, up = bq.merge_lora(pk1["lora_down"], pk1["lora_up"], pk1["smooth_inv"], a_bits, b_bits)
+    pk48 = dict(pk1, lora_down=down, lora_up=up)
+    L48 = bq.PackedLinear.from_host(pk48, lay1["bias"], down.shape[0], device=dev)
+    x1 = fc1[1]
+    out["fc1_lora_r48"] = time_layer(bq, torch, np, stream, L48, [x1, x1.clone()], x1.shape[0], reps=20)
+    del L48
+    # C0: tiny
+    st = synth.layer_spec("tiny")
+    lt = synth.gen_layer(st)
+    xt = to_dev_bf16(lt["x"])
+    axt = xt.float().abs().amax(dim=0).cpu().numpy().astype(np.float32)
+    Lt = bq.PackedLinear.from_host(bq.pack_weights(lt["w"], axt, st.rank), lt["bias"], st.rank, device=dev)
+    out["tiny"] = time_layer(bq, torch, np, stream, Lt, [xt], st.M, reps=50)
+    # per-GPU share of the MLP pair
+    for tag, (L, x) in (("fc1_m576", fc1), ("fc2_m576", fc2)):
+        xs_ = [x[:576].contiguous(), x[576:1152].contiguous()]
+        out[tag] = time_layer(bq, torch, np, stream, L, xs_, 576, reps=30)
+    log(f"bench: configs {json.dumps(out)}")
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_tiny(reps=5):
+    """The oracle's online path on the whole tiny case (256x512->512, rank
+    16): median of `reps` runs on all threads, and one run on one thread."""
+    import numpy as np
+    import oracle as O
+    import synth
+    st = synth.layer_spec("tiny")
+    lt = synth.gen_layer(st)
+    ax = np.abs(O.bf16_bits_to_f32(lt["x"])).max(axis=0).astype(np.float32)
+    pk = O.pack_weights(lt["w"], ax, st.rank)
+
+    def once():
+        t0 = time.perf_counter()
+        a = O.quantize_act_lora_down(lt["x"], pk["smooth_inv"], pk["l1"])
+        O.gemm_w4a4_lora_up(a["xq"], a["xs"], pk["wq"], pk["ws"], a["t"], pk["l2"], lt["bias"])
+        return time.perf_counter() - t0
+
+    ts = sorted(once() for _ in range(reps))
+    one = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            one = once()
+    except Exception:
+        pass
+    return {"us_median_of_5_all_threads": round(ts[len(ts) // 2] * 1e6, 1),
+            "us_one_thread": None if one is None else round(one * 1e6, 1)}
+
+
 def cpu_baseline(lay1, pk1, spec, seconds, chunk):
     """The oracle's online path (both fused kernels' steps) on whole chunks
     of fc1 token rows, spread over the token range, until `seconds` of host
@@ -553,7 +684,10 @@ def cpu_baseline(lay1, pk1, spec, seconds, chunk):
     dt = time.perf_counter() - t0
     ops = 2.0 * rows * spec.N * spec.K
     log(f"bench: cpu oracle {rows} rows of fc1 in {dt:.1f} s")
+    tiny = cpu_tiny()
+    log(f"bench: cpu oracle tiny case {json.dumps(tiny)}")
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(), "tiny_case": tiny,
             "sample": f"{rows} of {spec.M} token rows of fc1 ({spec.K}->{spec.N}, rank {spec.rank}) in "
                       f"chunks of {chunk}: quantize+down and per-group GEMM+up, {dt:.1f} s",
             "us_per_layer_equiv": round(dt / rows * spec.M * 1e6, 1)}
