@@ -433,6 +433,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, si
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n, 0x00020000);
 }
 
+// chunk swizzle of a 128-byte LDS row: over any 8 consecutive rows
+// (r0 = 0 mod 8) the swizzle takes all 8 values, and over any 16 (r0 = 0
+// mod 16) r mod 2 and the swizzle take all 16 combinations: the 16-byte
+// reads of consecutive rows at one chunk are conflict-free for 32 and for
+// 64 four-byte banks.
+__device__ __forceinline__ int swz8(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
+
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 buffer_load_u4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
@@ -689,7 +696,7 @@ __device__ __forceinline__ void load_bias(float (&bv)[2][4][4], const uint16_t* 
 // partial down projection x^2 . L1_2 over the tile's 128 columns, summed
 // into lact2 with fp32 atomics (lact2 cleared beforehand).
 // UPL: rank 32, and the tile's lora_act rows (128 x 32 fp32, 128-byte rows,
-// 16-byte chunk c of row r at chunk c ^ (r % 8)) and L2 rows (128 x 32 bf16
+// 16-byte chunk c of row r at chunk c ^ swz8(r)) and L2 rows (128 x 32 bf16
 // at byte 16384, 64-byte rows, chunk c of row r at c ^ ((r / 4) % 4)) are
 // already in LDS at upl.
 // PRE: the low-rank term and the bias are already in acc (lora_up_acc and
@@ -708,8 +715,8 @@ __device__ __forceinline__ void epilogue_tile128(v16f (&acc)[2][2], const StageT
       for (int jt = 0; jt < 2; ++jt) {
         const int r = wm * 64 + jt * 32 + l32;
         const uint8_t* row = upl + r * 128;
-        const float4 f0 = *reinterpret_cast<const float4*>(row + (((4 * c + 2 * h) ^ (r & 7)) << 4));
-        const float4 f1 = *reinterpret_cast<const float4*>(row + (((4 * c + 2 * h + 1) ^ (r & 7)) << 4));
+        const float4 f0 = *reinterpret_cast<const float4*>(row + (((4 * c + 2 * h) ^ swz8(r)) << 4));
+        const float4 f1 = *reinterpret_cast<const float4*>(row + (((4 * c + 2 * h + 1) ^ swz8(r)) << 4));
         ub[jt] = m0 + r < M ? v4i{static_cast<int>(pack_bf16_rne(f0.x, f0.y)), static_cast<int>(pack_bf16_rne(f0.z, f0.w)),
                                   static_cast<int>(pack_bf16_rne(f1.x, f1.y)), static_cast<int>(pack_bf16_rne(f1.z, f1.w))}
                             : v4i{0, 0, 0, 0};
@@ -810,7 +817,7 @@ __device__ __forceinline__ void upl_issue(uint8_t* dst, const float* __restrict_
   for (int j = 0; j < 4; ++j) {
     const int blk = 4 * wave + j, r = 8 * blk + (lane >> 3);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(dst + blk * 1024), 16,
-                                             r * 128 + (((lane & 7) ^ (r & 7)) << 4), 0, 0, 0);
+                                             r * 128 + (((lane & 7) ^ swz8(r)) << 4), 0, 0, 0);
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -842,7 +849,7 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_mxfp4(
   // Direct-to-LDS loads.  Waves 0, 1 load W rows, waves 2, 3 X rows: load j
   // of a wave fills rows 64 (wave % 2) + 8 j .. + 7 of its operand, lane i
   // row + i/8, 16-byte LDS chunk i%8, which holds the row's chunk
-  // (i%8) ^ (row%8) (the XOR spreads a column of rows over the banks).
+  // (i%8) ^ swz8(row) (the XOR spreads a column of rows over the banks).
   // Rows past the matrix edge are clamped to its last row; the resources
   // bound every access.
   const bool is_w = wave < 2;
@@ -855,7 +862,7 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_mxfp4(
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int r = lrow + 8 * j;
-    vcode[j] = min(r0 + r, rows - 1) * kb + (((lane & 7) ^ (r & 7)) << 4);
+    vcode[j] = min(r0 + r, rows - 1) * kb + (((lane & 7) ^ swz8(r)) << 4);
   }
   const int lds_op = is_w ? 0 : kMxdOp;
   // scales of a stage: 8 blocks x 128 rows = 256 dwords per operand; the
@@ -904,7 +911,8 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_mxfp4(
       for (int r = 0; r < 16; ++r) acc[it][jt][r] = 0.f;
 
   // 64-k substep s: logical chunk 2s + h of the row (block 2s + h of the
-  // stage), stored at chunk (2s + h) ^ (row % 8); row % 8 = l32 % 8
+  // stage), stored at chunk (2s + h) ^ swz8(row); swz8(row) = swz8(l32)
+  // (rows differ from l32 by multiples of 32)
   auto compute = [&](auto buf_c, bool half) {
     constexpr int buf = decltype(buf_c)::value;
     const uint8_t* wb = &lds_c[buf][0] + (wn * 64 + l32) * kMxdRowB;
@@ -913,7 +921,7 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_mxfp4(
     const uint8_t* xsc = &lds_c[buf][2 * kMxdOp + 8 * kTile] + wm * 64 + l32;
     auto sub = [&](auto s_c) {
       constexpr int s = decltype(s_c)::value;
-      const int ch = ((2 * s + h) ^ (l32 & 7)) << 4;
+      const int ch = ((2 * s + h) ^ swz8(l32)) << 4;
       v4i a[2], b[2];
       uint32_t sa[2], sb[2];
 #pragma unroll
