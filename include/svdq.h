@@ -294,8 +294,10 @@ SVDQ_API int svdq_unfused_linear_noalloc(const void* x, int M, int K,
 /* Measurement hook: the dense matrix-core rate this GPU sustains.  Each of
  * `blocks` workgroups (4 waves; launch two per CU) issues 8 * iters
  * independent v_mfma_scale_f32_32x32x64_f8f6f4 per wave, with FP8 operands
- * (precision SVDQ_INT4: the 8-bit rate the INT4 GEMM runs at) or FP4
- * operands (SVDQ_MXFP4).  Ops per launch = blocks * 4 * 8 * iters * 131072;
+ * (precision SVDQ_INT4: 16 passes per instruction, the matrix time the INT4
+ * GEMM spends per K-group and 32x32 tile as one 8-pass FP6 product plus one
+ * 8-pass rank-1 scale product) or FP4 operands (SVDQ_MXFP4).
+ * Ops per launch = blocks * 4 * 8 * iters * 131072;
  * the caller times it.  out (dev) [blocks] fp32 receives one checksum per
  * workgroup.  blocks, iters >= 1. */
 SVDQ_API int svdq_bench_mfma_ceiling(int precision, int blocks, int iters, float* out, void* stream);

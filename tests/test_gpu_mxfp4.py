@@ -118,16 +118,19 @@ def test_mx_k2_parity(p):
     assert_y_close(host_u16(y), ref["y"], "mx k2", sl, ref["y64"])
 
 
+@pytest.mark.parametrize("shape", [(133, 768, 136), (260, 768, 132)], ids=["ragged", "rows4"])
 @pytest.mark.parametrize("spread", [(120, 134), (100, 150), (0, 0)], ids=["near1", "wide", "zero"])
-def test_mx_k2_block_scales(spread):
+def test_mx_k2_block_scales(spread, shape):
     """Random codes with an independent random scale byte per 32-block of
     every row: a scale applied to the wrong block, row or lane half shows
     as a large error (checked per output row against that row's largest
-    value).  (0, 0): every scale is 2^-127 and every product underflows."""
+    value).  (0, 0): every scale is 2^-127 and every product underflows.
+    Row counts that are multiples of 4 load their scales as dwords of 4
+    rows, the others byte by byte at the ragged edge."""
     lo, hi = spread
-    say(f"mx k2 block scales {spread}")
+    say(f"mx k2 block scales {spread} {shape}")
     rng = np.random.default_rng([78, lo, hi])
-    M, K, N = 133, 768, 136
+    M, K, N = shape
     codes_x = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
     codes_w = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
     sx = rng.integers(lo, hi + 1, size=(K // 32, M)).astype(np.uint8)
