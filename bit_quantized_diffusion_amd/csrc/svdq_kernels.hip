@@ -1015,6 +1015,7 @@ constexpr int kI4Stage = 128;                    // k per pipeline stage (2 grou
 constexpr int kI4RowB = kI4Stage / 2;            // packed bytes per row and stage
 constexpr int kI4Op = kTile * kI4RowB;           // one operand's rows in a slot (8 KB)
 constexpr int kI4Slots = 3;                      // ring depth: loads run two stages ahead
+constexpr int kI4CoarseMinK = 8192;              // K from which the fused GEMM takes the coarse schedule
 // every slot's W rows and X rows are LDS arrays of their own (so that the
 // compiler tells a stage's reads from the loads landing in another slot and
 // waits for neither); slot 0's two arrays also hold the epilogue's output
@@ -1068,7 +1069,7 @@ __device__ __forceinline__ void lds_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
 }
 
-template <bool DEBUG, int EPI = 0>
+template <bool DEBUG, int EPI = 0, bool COARSE = false>
 __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
     const uint8_t* __restrict__ xq, const uint16_t* __restrict__ xs,
     const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
@@ -1254,13 +1255,21 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   using I2 = Slot<2>;
   using I3 = Slot<3>;
 
-  // A stage (one group on an odd-G last stage) as one software pipeline
-  // over its tile-groups: both MFMAs of tile-group t+1 (the FP6 product and
-  // the scale outer product) are issued before the dequant of tile-group t,
-  // so the FMAs find their operands done; the second group's chunks are read
-  // and converted while the first group computes.  The stage's last two tile-groups
-  // leave compute with their MFMAs in flight; their dequant (finish) runs
-  // after the stage barrier.
+  // A stage (one group on an odd-G last stage) runs its tile-groups in one
+  // of two schedules; in both the second group's chunks are read and
+  // converted while the first group computes, and the stage's last two
+  // tile-groups leave compute with their MFMAs in flight, their dequant
+  // (finish) running after the stage barrier.
+  //  - fine (default): both MFMAs of tile-group t+1 (the FP6 product and the
+  //    scale outer product) are issued before the dequant of tile-group t,
+  //    and the compiler interleaves MFMAs and FMAs freely;
+  //  - COARSE: the four MFMAs of two tile-groups back to back, then their 32
+  //    dequant FMAs and the other VALU work, with scheduling barriers between
+  //    the phases, so that with two waves per SIMD one wave's MFMA phase can
+  //    run under the other's VALU phase.  The two co-resident workgroups
+  //    start their tiles together; over a long K loop they settle out of
+  //    phase, over a short one they do not, so only long K loops take it.
+  // Per output element the FMAs run in the same order in both.
   v16f pa, pb, ca, cb;
   auto finish = [&]() __attribute__((always_inline)) {
     dqc(I2{}, pa, ca);
@@ -1296,6 +1305,42 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
       };
       group(I0{});
       if (!one) group(I1{});
+    } else if constexpr (COARSE) {
+      const Raw r0 = load_raw(slot, I0{});
+      const Scl c = load_scl(wslot);
+      pre();
+      const Ops o0 = cvt(r0);
+      __builtin_amdgcn_sched_barrier(0);
+      pa = mf(o0, c, I0{}, I0{});
+      ca = rk(c, I0{}, I0{});
+      pb = mf(o0, c, I0{}, I1{});
+      cb = rk(c, I0{}, I1{});
+      __builtin_amdgcn_sched_barrier(0);
+      dqc(I0{}, pa, ca);
+      dqc(I1{}, pb, cb);
+      __builtin_amdgcn_sched_barrier(0);
+      pa = mf(o0, c, I0{}, I2{});
+      ca = rk(c, I0{}, I2{});
+      pb = mf(o0, c, I0{}, I3{});
+      cb = rk(c, I0{}, I3{});
+      __builtin_amdgcn_sched_barrier(0);
+      if (one) return;
+      const Ops o1 = cvt(load_raw(slot, I1{}));
+      dqc(I2{}, pa, ca);
+      dqc(I3{}, pb, cb);
+      __builtin_amdgcn_sched_barrier(0);
+      pa = mf(o1, c, I1{}, I0{});
+      ca = rk(c, I1{}, I0{});
+      pb = mf(o1, c, I1{}, I1{});
+      cb = rk(c, I1{}, I1{});
+      __builtin_amdgcn_sched_barrier(0);
+      dqc(I0{}, pa, ca);
+      dqc(I1{}, pb, cb);
+      __builtin_amdgcn_sched_barrier(0);
+      pa = mf(o1, c, I1{}, I2{});
+      ca = rk(c, I1{}, I2{});
+      pb = mf(o1, c, I1{}, I3{});
+      cb = rk(c, I1{}, I3{});
     } else {
       const Raw r0 = load_raw(slot, I0{});
       const Scl c = load_scl(wslot);
@@ -1728,10 +1773,18 @@ extern "C" int svdq_launch_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs, 
                        static_cast<uint16_t*>(y), M, N, K, rank);
     return static_cast<int>(hipGetLastError());
   }
-  hipLaunchKernelGGL(k2_gemm_int4<false>, dim3(tiles), dim3(kMxThreads), 0, static_cast<hipStream_t>(stream), xq,
-                     static_cast<const uint16_t*>(xs), wq, static_cast<const uint16_t*>(ws), lora_act,
-                     static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias),
-                     static_cast<uint16_t*>(y), M, N, K, rank, 0, 0, 0, 0, nullptr, MlpOut{});
+  // long K loops take the coarse MFMA/VALU phases (see k2_gemm_int4)
+  if (K >= kI4CoarseMinK)
+    hipLaunchKernelGGL((k2_gemm_int4<false, 0, true>), dim3(tiles), dim3(kMxThreads), 0,
+                       static_cast<hipStream_t>(stream), xq, static_cast<const uint16_t*>(xs), wq,
+                       static_cast<const uint16_t*>(ws), lora_act, static_cast<const uint16_t*>(lora_up),
+                       static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), M, N, K, rank, 0, 0, 0, 0,
+                       nullptr, MlpOut{});
+  else
+    hipLaunchKernelGGL(k2_gemm_int4<false>, dim3(tiles), dim3(kMxThreads), 0, static_cast<hipStream_t>(stream), xq,
+                       static_cast<const uint16_t*>(xs), wq, static_cast<const uint16_t*>(ws), lora_act,
+                       static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias),
+                       static_cast<uint16_t*>(y), M, N, K, rank, 0, 0, 0, 0, nullptr, MlpOut{});
   return static_cast<int>(hipGetLastError());
 }
 

@@ -80,6 +80,8 @@ SMALL = [
     (64, 256, 64, 64, 4, False),
     (520, 1024, 264, 16, 5, True),
     (40, 4096, 272, 256, 6, True),    # largest rank
+    (136, 8192, 144, 16, 7, True),    # long K loop: the fused GEMM's coarse schedule
+    (72, 8256, 136, 32, 8, True),     # long K loop, odd group count
 ]
 
 
