@@ -1266,9 +1266,9 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   //  - COARSE: the four MFMAs of two tile-groups back to back, then their 32
   //    dequant FMAs and the other VALU work, with scheduling barriers between
   //    the phases, so that with two waves per SIMD one wave's MFMA phase can
-  //    run under the other's VALU phase.  The two co-resident workgroups
-  //    start their tiles together; over a long K loop they settle out of
-  //    phase, over a short one they do not, so only long K loops take it.
+  //    run under the other's VALU phase.  Measured on FLUX's MLP layers it
+  //    is faster over a 96-stage K loop and slower over a 24-stage one, so
+  //    only long K loops take it.
   // Per output element the FMAs run in the same order in both.
   v16f pa, pb, ca, cb;
   auto finish = [&]() __attribute__((always_inline)) {
