@@ -1382,11 +1382,13 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   // stage st+2 still out), it splits stage st+1's scales, and it ends with
   // stage st+1 complete (at most stage st+2's six loads out) and the
   // barrier.
-  // Prologue: stages 0 and 1 in flight; meanwhile the tile's low-rank term
-  // and bias go into the accumulators (the main loop adds the 4-bit
-  // products to them); then stage 0 complete and split.
+  // Prologue: stage 0 in flight; meanwhile the tile's low-rank term and
+  // bias go into the accumulators (the main loop adds the 4-bit products to
+  // them).  Stage 1 is issued only after that, so that the compiler's wait
+  // for the low-rank operands (it counts only its own loads, hence waits
+  // for every load issued before them) does not also wait for stage 1;
+  // then stage 0 complete and split.
   dma(0, Slot<0>{});
-  if (S > 1) dma(1, Slot<1>{});
   if constexpr (!DEBUG) {
     lora_up_acc(acc, lact, lup, M, N, rank, n0, m0, wn, wm, l32, h);
     float bv[2][4][4];
@@ -1398,6 +1400,7 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[it][jt][r] += bv[it][r / 4][r % 4];
   }
+  if (S > 1) dma(1, Slot<1>{});
   if (S > 1)
     vm_wait<6>();
   else
