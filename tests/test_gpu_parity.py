@@ -82,6 +82,9 @@ SMALL = [
     (40, 4096, 272, 256, 6, True),    # largest rank
     (136, 8192, 144, 16, 7, True),    # long K loop: the fused GEMM's coarse schedule
     (72, 8256, 136, 32, 8, True),     # long K loop, odd group count
+    (130, 64, 150, 16, 9, True),      # one group (one half stage) with the low-rank branch
+    (257, 128, 129, 32, 10, False),   # one stage, ragged M and N
+    (33, 8192, 131, 16, 11, True),    # coarse schedule with odd N (element stores)
 ]
 
 
