@@ -189,3 +189,30 @@ def test_mx_full_size_fc1():
     ref = C.mx_oracle_rows(case, rows)
     sl = C.mx_slack(ref["xq"], ref["xs"], pk["wq"], pk["ws"], ref["t"], pk["l2"], case["bias"], t_from_kernel=True)
     assert_y_close(host_u16(y)[rows], ref["y"], "mx fc1 end to end", sl, ref["y64"])
+
+
+def test_mx_full_size_fc2():
+    """FLUX fc2 (4608 x 12288 -> 3072, rank 32, input bf16(GELU(fc1's Y)))
+    in MXFP4: codes and scales of every row bit-exact, Y on sampled rows."""
+    say("mx full-size fc2: building oracle case")
+    case = C.mlp_pair()[1]
+    pk = C.mx_pack(case)
+    r = case["rank"]
+    M, K = case["x"].shape
+    N = pk["wq"].shape[0]
+    say(f"mx full-size fc2: M={M} K={K} N={N} rank={r}")
+    layer = _mx_layer(case, pk)
+    x = dev_bf16(case["x"])
+    xq, xs, la = bq.quantize_act_lora_down(x, layer.smooth_inv, layer.lora_down, r, bq.MXFP4)
+    y = bq.gemm_w4a4_lora_up(xq, xs, layer.wq, layer.ws, la, layer.lora_up, layer.bias, M, N, K, r, bq.MXFP4)
+    torch.cuda.synchronize()
+    ref_a = O.mx_quantize_act_lora_down(case["x"], pk["smooth_inv"], pk["l1"])
+    assert np.array_equal(xq.cpu().numpy(), ref_a["xq"])
+    assert np.array_equal(xs.cpu().numpy(), ref_a["xs"])
+    t = ref_a["t"]
+    assert np.allclose(la.cpu().numpy().astype(np.float64), t, rtol=1e-3, atol=1e-4 * np.max(np.abs(t)))
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, M - 1], rng.choice(M, 27, replace=False)]))
+    ref = C.mx_oracle_rows(case, rows)
+    sl = C.mx_slack(ref["xq"], ref["xs"], pk["wq"], pk["ws"], ref["t"], pk["l2"], case["bias"], t_from_kernel=True)
+    assert_y_close(host_u16(y)[rows], ref["y"], "mx fc2 end to end", sl, ref["y64"])

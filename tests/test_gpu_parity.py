@@ -359,6 +359,29 @@ def test_full_size_layer(name):
     assert_y_close(host_u16(y)[rows], ref["y"], f"{name} end to end", sl, ref["y64"])
 
 
+@pytest.mark.parametrize("name", ["fc1", "fc2"])
+def test_per_gpu_share_every_row(name):
+    """The FLUX MLP layers at M = 576, the token rows each of eight GPUs
+    holds when the 4608 rows are split (fc2's 120 tiles fill under a
+    quarter of the workgroup slots): codes, scales and Y of every row
+    against the oracle."""
+    case = _full_case(name)
+    pk, r = case["pk"], case["rank"]
+    M, K = 576, case["x"].shape[1]
+    N = pk["wq"].shape[0]
+    say(f"per-GPU share {name}: M={M} K={K} N={N} rank={r}")
+    layer = device_layer(case)
+    x = dev_bf16(case["x"][:M])
+    xq, xs, la = bq.quantize_act_lora_down(x, layer.smooth_inv, layer.lora_down, r)
+    y = bq.gemm_w4a4_lora_up(xq, xs, layer.wq, layer.ws, la, layer.lora_up, layer.bias, M, N, K, r)
+    torch.cuda.synchronize()
+    ref = C.oracle_rows(case, np.arange(M))
+    assert np.array_equal(xq.cpu().numpy(), ref["xq"])
+    assert np.array_equal(host_u16(xs), ref["xs"].view(np.uint16))
+    sl = C.int4_slack(ref, ref["xs"], pk["ws"], ref["t"], pk["l2"], case["bias"], t_from_kernel=True)
+    assert_y_close(host_u16(y), ref["y"], f"{name} M=576", sl, ref["y64"])
+
+
 def test_layer_with_merged_lora():
     """A rank-32 layer with a rank-16 adapter merged by the library's host
     call (svdq_merge_lora): the rank-48 hot path against the oracle of the
