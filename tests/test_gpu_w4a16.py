@@ -106,3 +106,17 @@ def test_w4a16_full_size_fc1():
     rows = np.unique(np.concatenate([[0, 1, 127, 128, M - 1], rng.choice(M, 27, replace=False)]))
     ref = O.w4a16_linear(case["x"][rows], wq, ws, case["bias"])
     assert_y_close(got[rows], ref["y"], "w4a16 fc1")
+
+
+def test_w4a16_full_size_fc2():
+    """FLUX fc2 (4608 x 12288 -> 3072, input bf16(GELU(fc1's Y))) in W4A16:
+    sampled rows against the oracle."""
+    say("w4a16 full-size fc2: building case")
+    case = C.mlp_pair()[1]
+    wq, ws = O.pack_w4a16(case["w"])
+    M = case["x"].shape[0]
+    got = _run(case, wq, ws)
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, M - 1], rng.choice(M, 27, replace=False)]))
+    ref = O.w4a16_linear(case["x"][rows], wq, ws, case["bias"])
+    assert_y_close(got[rows], ref["y"], "w4a16 fc2")
