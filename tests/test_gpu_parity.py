@@ -292,6 +292,30 @@ def test_unfused_baseline(p):
     assert_y_close(host_u16(y), ref["y"], "unfused", sl, ref["y64"])
 
 
+@pytest.mark.parametrize("name", ["fc1", "fc2"])
+def test_unfused_baseline_full_size(name):
+    """The four-kernel baseline on the FLUX MLP layers the fusion ablation
+    times: codes and scales equal to the fused path's on every row, Y on
+    sampled rows against the oracle (bound as in the small-shape test)."""
+    case = _full_case(name)
+    pk = case["pk"]
+    M = case["x"].shape[0]
+    say(f"unfused full-size {name}")
+    layer = device_layer(case)
+    x = dev_bf16(case["x"])
+    xq_u = torch.empty((M, x.shape[1] // 2), dtype=torch.uint8, device=x.device)
+    xs_u = torch.empty((x.shape[1] // 64, M), dtype=torch.float16, device=x.device)
+    y = bq.unfused_linear(x, layer, xq=xq_u, xs=xs_u)
+    xq, xs, _ = bq.quantize_act_lora_down(x, layer.smooth_inv, layer.lora_down, layer.rank)
+    torch.cuda.synchronize()
+    assert torch.equal(xq, xq_u) and torch.equal(xs.view(torch.int16), xs_u.view(torch.int16))
+    rows = _sample_rows(M, seed=3)
+    ref = C.oracle_rows(case, rows)
+    sl = C.int4_slack(ref, ref["xs"], pk["ws"], ref["t"], pk["l2"], case["bias"], t_from_kernel=True)
+    sl = sl + 0.5 * C.ulp_bf16(np.abs(ref["acc"]) + sl)
+    assert_y_close(host_u16(y)[rows], ref["y"], f"unfused {name}", sl, ref["y64"])
+
+
 def test_outputs_reused_buffers_and_streams():
     """Caller-owned outputs are written in place; a side stream works."""
     case = _small(SMALL[1])
