@@ -182,22 +182,59 @@ def quantize_act_lora_down(x, smooth_inv, lora_down, rank: int, precision: int =
     return xq, xs, (lora_act if rank else None)
 
 
+def gemm_workspace_size(M: int, N: int, K: int, precision: int = INT4) -> int:
+    """Bytes of workspace svdq_gemm_w4a4_lora_up_ws can use for this shape
+    on the current device (0: the single-pass schedule runs anyway)."""
+    out = ctypes.c_size_t(0)
+    check(lib.svdq_gemm_workspace_size(M, N, K, precision, ctypes.byref(out)))
+    return int(out.value)
+
+
+_WS_BYTES = {}
+
+
+def _workspace_bytes(dev, M, N, K, precision):
+    """gemm_workspace_size, asked once per device and shape (the answer
+    depends on nothing else), so that the per-call cost is a lookup."""
+    key = (dev.index, M, N, K, precision)
+    n = _WS_BYTES.get(key)
+    if n is None:
+        n = _WS_BYTES[key] = gemm_workspace_size(M, N, K, precision)
+    return n
+
+
 def gemm_w4a4_lora_up(xq, xs, wq, ws, lora_act, lora_up, bias, M: int, N: int, K: int,
-                      rank: int, precision: int = INT4, y=None):
-    """Second fused kernel.  Returns y bf16 [M][N]."""
+                      rank: int, precision: int = INT4, y=None, workspace="auto"):
+    """Second fused kernel.  Returns y bf16 [M][N].
+
+    workspace: "auto" allocates (from torch's allocator, on the call's
+    stream) the bytes gemm_workspace_size asks for, so that grids that would
+    leave the device mostly idle run split along K; None calls the entry
+    point without a workspace (single-pass schedule); a uint8 device tensor
+    is used as given."""
     torch = _torch()
     dev = xq.device
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     sd = _scale_dtype(precision)
-    check(lib.svdq_gemm_w4a4_lora_up(
-        _dptr(xq, torch.uint8, (M, K // 2), "xq"), _dptr(xs, sd, _scale_shape(K, M, precision), "xs"),
-        _dptr(wq, torch.uint8, (N, K // 2), "wq"), _dptr(ws, sd, _scale_shape(K, N, precision), "ws"),
-        _dptr(lora_act, torch.float32, (M, rank), "lora_act") if rank else None,
-        _dptr(lora_up, torch.bfloat16, (N, rank), "lora_up") if rank else None,
-        _dptr(bias, torch.bfloat16, (N,), "bias"),
-        _dptr(y, torch.bfloat16, (M, N), "y"),
-        M, N, K, rank, precision, _stream(dev)))
+    args = (_dptr(xq, torch.uint8, (M, K // 2), "xq"), _dptr(xs, sd, _scale_shape(K, M, precision), "xs"),
+            _dptr(wq, torch.uint8, (N, K // 2), "wq"), _dptr(ws, sd, _scale_shape(K, N, precision), "ws"),
+            _dptr(lora_act, torch.float32, (M, rank), "lora_act") if rank else None,
+            _dptr(lora_up, torch.bfloat16, (N, rank), "lora_up") if rank else None,
+            _dptr(bias, torch.bfloat16, (N,), "bias"),
+            _dptr(y, torch.bfloat16, (M, N), "y"),
+            M, N, K, rank, precision)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
+        nbytes = _workspace_bytes(dev, M, N, K, precision)
+        workspace = torch.empty((nbytes,), dtype=torch.uint8, device=dev) if nbytes else None
+    if workspace is None:
+        check(lib.svdq_gemm_w4a4_lora_up(*args, _stream(dev)))
+    else:
+        n = workspace.numel()
+        check(lib.svdq_gemm_w4a4_lora_up_ws(*args, _dptr(workspace, torch.uint8, (n,), "workspace"), n,
+                                            _stream(dev)))
     return y
 
 

@@ -28,7 +28,7 @@ EXPORTED = (
     "svdq_unfused_linear", "svdq_debug_group_partials", "svdq_merge_lora",
     "svdq_gemm_w4a4_lora_up_gelu", "svdq_mlp_gemm_gelu_quant",
     "svdq_pack_w4a16", "svdq_gemm_w4a16", "svdq_bench_mfma_ceiling",
-    "svdq_unfused_linear_noalloc",
+    "svdq_unfused_linear_noalloc", "svdq_gemm_workspace_size", "svdq_gemm_w4a4_lora_up_ws",
 )
 
 
@@ -69,6 +69,8 @@ def _load():
         "svdq_gemm_w4a16": ([vp, vp, vp, vp, vp, i, i, i, vp], i),
         "svdq_bench_mfma_ceiling": ([i, i, i, vp, vp], i),
         "svdq_unfused_linear_noalloc": ([vp, i, i, vp, vp, i, vp, vp, vp, vp, i, i, vp, vp], i),
+        "svdq_gemm_workspace_size": ([i, i, i, i, sz], i),
+        "svdq_gemm_w4a4_lora_up_ws": ([vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, ctypes.c_size_t, vp], i),
     }
     for name, (args, ret) in sig.items():
         fn = getattr(lib, name)

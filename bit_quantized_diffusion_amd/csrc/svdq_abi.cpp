@@ -145,6 +145,41 @@ int svdq_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs, const uint8_t* wq,
                                                   precision, stream));
 }
 
+int svdq_gemm_workspace_size(int M, int N, int K, int precision, size_t* out_bytes) {
+  int st = check_precision(precision);
+  if (st) return st;
+  if (!out_bytes) return SVDQ_ERR_INVALID_ARG;
+  *out_bytes = 0;
+  if (M < 1 || N < 1) return SVDQ_ERR_SHAPE;
+  if ((st = check_k(K, precision))) return st;
+  if ((st = check_operand_extent(M, K, precision)) || (st = check_operand_extent(N, K, precision))) return st;
+  if ((st = current_device_ok())) return st;
+  int splits = 1, per = 0;
+  svdq_gemm_split_plan(M, N, K, precision, &splits, &per, out_bytes);
+  return SVDQ_OK;
+}
+
+int svdq_gemm_w4a4_lora_up_ws(const uint8_t* xq, const void* xs, const uint8_t* wq, const void* ws,
+                              const float* lora_act, const void* lora_up, const void* bias, void* y, int M, int N,
+                              int K, int rank, int precision, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_precision(precision);
+  if (st) return st;
+  if (!xq || !xs || !wq || !ws || !y) return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!lora_act || !lora_up)) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(wq) || !aligned16(ws) || !aligned16(y))
+    return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!aligned16(lora_act) || !aligned16(lora_up))) return SVDQ_ERR_INVALID_ARG;
+  if (bias && !aligned16(bias)) return SVDQ_ERR_INVALID_ARG;
+  if (workspace && !aligned16(workspace)) return SVDQ_ERR_INVALID_ARG;
+  if (M < 1 || N < 1) return SVDQ_ERR_SHAPE;
+  if ((st = check_k(K, precision))) return st;
+  if ((st = check_rank(rank, K, N))) return st;
+  if ((st = check_operand_extent(M, K, precision)) || (st = check_operand_extent(N, K, precision))) return st;
+  if ((st = current_device_ok())) return st;
+  return hip_status(svdq_launch_gemm_w4a4_lora_up_ws(xq, xs, wq, ws, lora_act, lora_up, bias, y, M, N, K, rank,
+                                                     precision, workspace, workspace_bytes, stream));
+}
+
 int svdq_gemm_w4a4_lora_up_gelu(const uint8_t* xq, const void* xs, const uint8_t* wq, const void* ws,
                                 const float* lora_act, const void* lora_up, const void* bias, void* y, int M, int N,
                                 int K, int rank, int precision, void* stream) {

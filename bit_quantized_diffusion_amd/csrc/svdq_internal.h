@@ -57,6 +57,13 @@ int svdq_launch_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs,
                                   const void* bias, void* y, int M, int N,
                                   int K, int rank, int precision,
                                   void* stream);
+// Split-K plan of svdq_launch_gemm_w4a4_lora_up_ws for the current device
+// (splits = 1 and bytes = 0 when the single-pass schedule runs); returns 0.
+int svdq_gemm_split_plan(int M, int N, int K, int precision, int* splits, int* per, size_t* bytes);
+int svdq_launch_gemm_w4a4_lora_up_ws(const uint8_t* xq, const void* xs, const uint8_t* wq, const void* ws,
+                                     const float* lora_act, const void* lora_up, const void* bias, void* y, int M,
+                                     int N, int K, int rank, int precision, void* workspace, size_t workspace_bytes,
+                                     void* stream);
 int svdq_launch_gemm_int4_gelu(const uint8_t* xq, const void* xs, const uint8_t* wq, const void* ws,
                                const float* lora_act, const void* lora_up, const void* bias, void* y, int M, int N,
                                int K, int rank, void* stream);

@@ -1069,13 +1069,24 @@ __device__ __forceinline__ void lds_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
 }
 
+// Split-K (EPI = kEpiPartial): block (tile, y) computes stages
+// [y per, min(S, (y + 1) per)) of the tile and writes its fp32 accumulators
+// to part[(y * tiles + tile) * 4096 + i * 256 + thread], i = 0..15 (the
+// thread's 64 values in accumulator order); the low-rank term, the bias and
+// the rounding are left to k_splitk_finish.
+constexpr int kEpiPartial = 3;
+struct SplitOut {
+  float4* part;
+  int per;
+};
+
 template <bool DEBUG, int EPI = 0, bool COARSE = false>
 __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
     const uint8_t* __restrict__ xq, const uint16_t* __restrict__ xs,
     const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
     const float* __restrict__ lact, const uint16_t* __restrict__ lup,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N, int K, int rank,
-    int win_m0, int win_n0, int win_mt, int win_nt, int32_t* __restrict__ dbg, MlpOut mo) {
+    int win_m0, int win_n0, int win_mt, int win_nt, int32_t* __restrict__ dbg, MlpOut mo, SplitOut so) {
   __shared__ __attribute__((aligned(16))) uint8_t w_ring0[kI4Half];
   __shared__ __attribute__((aligned(16))) uint8_t x_ring0[kI4Half];
   __shared__ __attribute__((aligned(16))) uint8_t w_ring1[kI4Op];
@@ -1100,6 +1111,10 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   const int G = K / 64;
   const int S = (G + 1) / 2;                   // the last stage holds one group when G is odd
   const int kb = K / 2;
+  // the stages this block computes: [s_lo, s_lo + SL) (all of them but in
+  // the split-K pass)
+  const int s_lo = EPI == kEpiPartial ? static_cast<int>(blockIdx.y) * so.per : 0;
+  const int SL = EPI == kEpiPartial ? min(so.per, S - s_lo) : S;
 
   int n0, m0;
   if constexpr (DEBUG) {
@@ -1140,12 +1155,13 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   const int vs = 2 * min((op == 0 ? n0 : m0) + s_row, s_rows - 1);
   auto dma = [&](int st, auto slot_c) __attribute__((always_inline)) {
     constexpr int slot = decltype(slot_c)::value;
-    const int sso = 2 * st * gbytes;
+    const int gst = s_lo + st;                 // the stage's index in the tile's K loop
+    const int sso = 2 * gst * gbytes;
     dma_u16(rs, lds_addr(&s_raw[st & 1][op][0][64 * (wave & 1)]), vs, sso);
     dma_u16(rs, lds_addr(&s_raw[st & 1][op][1][64 * (wave & 1)]), vs, sso + gbytes);
     const uint8_t* base = (op == 0 ? wring(slot) : xring(slot)) + 64 * (wave & 1) * kI4RowB;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma_b128(rc, lds_addr(base + 16 * j * kI4RowB), vcode[j], st * kI4RowB);
+    for (int j = 0; j < 4; ++j) dma_b128(rc, lds_addr(base + 16 * j * kI4RowB), vcode[j], gst * kI4RowB);
   };
   // A scale s (fp16 >= 0) splits as s = m 2^e with m in [0.5, 1)
   // (v_frexp_mant_f16, v_frexp_exp_i16_f16, subnormals included; s == 0
@@ -1389,7 +1405,7 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   // for every load issued before them) does not also wait for stage 1;
   // then stage 0 complete and split.
   dma(0, Slot<0>{});
-  if constexpr (!DEBUG) {
+  if constexpr (!DEBUG && EPI != kEpiPartial) {
     lora_up_acc(acc, lact, lup, M, N, rank, n0, m0, wn, wm, l32, h);
     float bv[2][4][4];
     load_bias(bv, bias, N, n0, wn, h);
@@ -1400,8 +1416,8 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[it][jt][r] += bv[it][r / 4][r % 4];
   }
-  if (S > 1) dma(1, Slot<1>{});
-  if (S > 1)
+  if (SL > 1) dma(1, Slot<1>{});
+  if (SL > 1)
     vm_wait<6>();
   else
     vm_wait<0>();
@@ -1410,13 +1426,13 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   auto iteration = [&](int st, auto slot_c) __attribute__((always_inline)) {
     constexpr int slot = decltype(slot_c)::value;
     constexpr int slot2 = (slot + 2) % kI4Slots;
-    const bool ahead = st + 2 < S;             // uniform
-    compute(slot, st & 1, 2 * st + 1 >= G, 2 * st, [&]() __attribute__((always_inline)) {
+    const bool ahead = st + 2 < SL;            // uniform
+    compute(slot, st & 1, 2 * (s_lo + st) + 1 >= G, 2 * st, [&]() __attribute__((always_inline)) {
       if (ahead) dma(st + 2, Slot<slot2>{});
       if constexpr (!DEBUG)
         if (st > 0) finish();
     });
-    if (st + 1 < S) {
+    if (st + 1 < SL) {
       if (ahead)
         vm_wait<10>();
       else
@@ -1428,16 +1444,71 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
     else
       lds_wait_barrier<0>();
   };
-  for (int st = 0; st < S; st += 3) {
+  for (int st = 0; st < SL; st += 3) {
     iteration(st, Slot<0>{});
-    if (st + 1 < S) iteration(st + 1, Slot<1>{});
-    if (st + 2 < S) iteration(st + 2, Slot<2>{});
+    if (st + 1 < SL) iteration(st + 1, Slot<1>{});
+    if (st + 2 < SL) iteration(st + 2, Slot<2>{});
   }
 
   if constexpr (!DEBUG) finish();
-  if constexpr (!DEBUG)
+  if constexpr (EPI == kEpiPartial) {
+    float4* dst = so.part + (static_cast<size_t>(blockIdx.y) * gridDim.x + blockIdx.x) * 4096 + tid;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const v16f& a = acc[i >> 3][(i >> 2) & 1];
+      const int r = 4 * (i & 3);
+      dst[i * 256] = make_float4(a[r], a[r + 1], a[r + 2], a[r + 3]);
+    }
+  } else if constexpr (!DEBUG) {
     epilogue_tile128<EPI, false, true>(acc, StageTile{reinterpret_cast<uint16_t*>(w_ring0), reinterpret_cast<uint16_t*>(x_ring0)}, lact,
                           lup, bias, y, M, N, rank, n0, m0, wn, wm, l32, h, tid, mo);
+  }
+}
+
+// Second pass of the split-K schedule: the splits' fp32 partials of a tile
+// summed in split order, then the shared epilogue (the up projection on the
+// accumulators, the bias, one rounding to bf16, full-line stores).
+__global__ __launch_bounds__(kMxThreads) void k_splitk_finish(const float4* __restrict__ part, int splits,
+                                                         const float* __restrict__ lact,
+                                                         const uint16_t* __restrict__ lup,
+                                                         const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
+                                                         int M, int N, int rank) {
+  __shared__ __attribute__((aligned(16))) uint16_t stg_lo[64 * kMxYRow];
+  __shared__ __attribute__((aligned(16))) uint16_t stg_hi[64 * kMxYRow];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+  const int wn = wave >> 1, wm = wave & 1;
+  const TileCoord tc = tile_coord(blockIdx.x, (N + kTile - 1) / kTile, (M + kTile - 1) / kTile);
+  v16f acc[2][2];
+  const float4* src = part + static_cast<size_t>(blockIdx.x) * 4096 + tid;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float4 v = src[i * 256];
+    v16f& a = acc[i >> 3][(i >> 2) & 1];
+    const int r = 4 * (i & 3);
+    a[r] = v.x;
+    a[r + 1] = v.y;
+    a[r + 2] = v.z;
+    a[r + 3] = v.w;
+  }
+  for (int sp = 1; sp < splits; ++sp) {
+    src += static_cast<size_t>(gridDim.x) * 4096;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float4 v = src[i * 256];
+      v16f& a = acc[i >> 3][(i >> 2) & 1];
+      const int r = 4 * (i & 3);
+      a[r] += v.x;
+      a[r + 1] += v.y;
+      a[r + 2] += v.z;
+      a[r + 3] += v.w;
+    }
+  }
+  epilogue_tile128<0>(acc, StageTile{stg_lo, stg_hi}, lact, lup, bias, y, M, N, rank, tc.n0, tc.m0, wn, wm, l32, h,
+                      tid, MlpOut{});
 }
 
 // ---------------------------------------------------------------------------
@@ -1692,7 +1763,7 @@ hipError_t launch_unfused(const void* x, int M, int K, const float* sinv, const 
   const int tiles = ((N + kTile - 1) / kTile) * ((M + kTile - 1) / kTile);               // 3: 4-bit GEMM
   hipLaunchKernelGGL(k2_gemm_int4<false>, dim3(tiles), dim3(kMxThreads), 0, st, xq, static_cast<const uint16_t*>(xs),
                      wq, static_cast<const uint16_t*>(ws), nullptr, nullptr, nullptr, static_cast<uint16_t*>(y), M, N,
-                     K, 0, 0, 0, 0, 0, nullptr, MlpOut{});
+                     K, 0, 0, 0, 0, 0, nullptr, MlpOut{}, SplitOut{});
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_up_proj, dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, st, lact,  // 4: up projection
                      static_cast<const uint16_t*>(lup), static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y),
@@ -1782,12 +1853,74 @@ extern "C" int svdq_launch_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs, 
                        static_cast<hipStream_t>(stream), xq, static_cast<const uint16_t*>(xs), wq,
                        static_cast<const uint16_t*>(ws), lora_act, static_cast<const uint16_t*>(lora_up),
                        static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), M, N, K, rank, 0, 0, 0, 0,
-                       nullptr, MlpOut{});
+                       nullptr, MlpOut{}, SplitOut{});
   else
     hipLaunchKernelGGL(k2_gemm_int4<false>, dim3(tiles), dim3(kMxThreads), 0, static_cast<hipStream_t>(stream), xq,
                        static_cast<const uint16_t*>(xs), wq, static_cast<const uint16_t*>(ws), lora_act,
                        static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias),
-                       static_cast<uint16_t*>(y), M, N, K, rank, 0, 0, 0, 0, nullptr, MlpOut{});
+                       static_cast<uint16_t*>(y), M, N, K, rank, 0, 0, 0, 0, nullptr, MlpOut{}, SplitOut{});
+  return static_cast<int>(hipGetLastError());
+}
+
+// Split-K plan of the fused INT4 GEMM for the current device: a grid whose
+// tiles fill under half the workgroup slots (two per CU) and whose K loop
+// is long (at least kSplitMinStages stages of 128 k) is cut along K into
+// `splits` runs of `per` stages (each at least 8); otherwise splits = 1.
+constexpr int kSplitMinStages = 16;
+constexpr int kSplitMax = 8;
+extern "C" int svdq_gemm_split_plan(int M, int N, int K, int precision, int* splits, int* per, size_t* bytes) {
+  *splits = 1;
+  *per = 0;
+  *bytes = 0;
+  if (precision != SVDQ_INT4) return 0;
+  static int slots_of[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (slots_of[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return 0;
+    slots_of[dev] = 2 * cus;
+  }
+  const int slots = slots_of[dev];
+  const int tiles = ((N + kTile - 1) / kTile) * ((M + kTile - 1) / kTile);
+  const int S = (K / 64 + 1) / 2;
+  if (2 * tiles > slots || S < kSplitMinStages) return 0;
+  int sp = min(min(slots / tiles, S / 8), kSplitMax);
+  if (sp < 2) return 0;
+  const int p = (S + sp - 1) / sp;
+  sp = (S + p - 1) / p;
+  *splits = sp;
+  *per = p;
+  *bytes = static_cast<size_t>(sp) * static_cast<size_t>(tiles) * 4096 * sizeof(float4);
+  return 0;
+}
+
+extern "C" int svdq_launch_gemm_w4a4_lora_up_ws(const uint8_t* xq, const void* xs, const uint8_t* wq, const void* ws,
+                                                const float* lora_act, const void* lora_up, const void* bias, void* y,
+                                                int M, int N, int K, int rank, int precision, void* workspace,
+                                                size_t workspace_bytes, void* stream) {
+  int splits = 1, per = 0;
+  size_t need = 0;
+  svdq_gemm_split_plan(M, N, K, precision, &splits, &per, &need);
+  if (splits < 2 || workspace == nullptr || workspace_bytes < need)
+    return svdq_launch_gemm_w4a4_lora_up(xq, xs, wq, ws, lora_act, lora_up, bias, y, M, N, K, rank, precision, stream);
+  const int tiles = ((N + kTile - 1) / kTile) * ((M + kTile - 1) / kTile);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float4* part = static_cast<float4*>(workspace);
+  const SplitOut so{part, per};
+  if (K >= kI4CoarseMinK)
+    hipLaunchKernelGGL((k2_gemm_int4<false, kEpiPartial, true>), dim3(tiles, splits), dim3(kMxThreads), 0, st, xq,
+                       static_cast<const uint16_t*>(xs), wq, static_cast<const uint16_t*>(ws), nullptr, nullptr,
+                       nullptr, static_cast<uint16_t*>(y), M, N, K, 0, 0, 0, 0, 0, nullptr, MlpOut{}, so);
+  else
+    hipLaunchKernelGGL((k2_gemm_int4<false, kEpiPartial, false>), dim3(tiles, splits), dim3(kMxThreads), 0, st, xq,
+                       static_cast<const uint16_t*>(xs), wq, static_cast<const uint16_t*>(ws), nullptr, nullptr,
+                       nullptr, static_cast<uint16_t*>(y), M, N, K, 0, 0, 0, 0, 0, nullptr, MlpOut{}, so);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return static_cast<int>(e);
+  hipLaunchKernelGGL(k_splitk_finish, dim3(tiles), dim3(kMxThreads), 0, st, part, splits, lora_act,
+                     static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias),
+                     static_cast<uint16_t*>(y), M, N, rank);
   return static_cast<int>(hipGetLastError());
 }
 
@@ -1798,7 +1931,7 @@ extern "C" int svdq_launch_gemm_int4_gelu(const uint8_t* xq, const void* xs, con
   hipLaunchKernelGGL((k2_gemm_int4<false, 1>), dim3(tiles), dim3(kMxThreads), 0, static_cast<hipStream_t>(stream), xq,
                      static_cast<const uint16_t*>(xs), wq, static_cast<const uint16_t*>(ws), lora_act,
                      static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias),
-                     static_cast<uint16_t*>(y), M, N, K, rank, 0, 0, 0, 0, nullptr, MlpOut{});
+                     static_cast<uint16_t*>(y), M, N, K, rank, 0, 0, 0, 0, nullptr, MlpOut{}, SplitOut{});
   return static_cast<int>(hipGetLastError());
 }
 
@@ -1818,7 +1951,7 @@ extern "C" int svdq_launch_mlp_gemm_gelu_quant(const uint8_t* xq, const void* xs
   hipLaunchKernelGGL((k2_gemm_int4<false, 2>), dim3(tiles), dim3(kMxThreads), 0, st, xq,
                      static_cast<const uint16_t*>(xs), wq, static_cast<const uint16_t*>(ws), lora_act,
                      static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias), nullptr, M, N, K, rank,
-                     0, 0, 0, 0, nullptr, mo);
+                     0, 0, 0, 0, nullptr, mo, SplitOut{});
   return static_cast<int>(hipGetLastError());
 }
 
@@ -1866,7 +1999,8 @@ extern "C" int svdq_launch_debug_group_partials(const uint8_t* xq, const uint8_t
                                                 int n0, int mt, int nt, int32_t* out, void* stream) {
   const int tiles = ((nt + kTile - 1) / kTile) * ((mt + kTile - 1) / kTile);
   hipLaunchKernelGGL(k2_gemm_int4<true>, dim3(tiles), dim3(kMxThreads), 0, static_cast<hipStream_t>(stream), xq,
-                     nullptr, wq, nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, 0, m0, n0, mt, nt, out, MlpOut{});
+                     nullptr, wq, nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, 0, m0, n0, mt, nt, out, MlpOut{},
+                     SplitOut{});
   return static_cast<int>(hipGetLastError());
 }
 

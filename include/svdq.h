@@ -202,6 +202,33 @@ SVDQ_API int svdq_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs,
                            int M, int N, int K, int rank, int precision,
                            void* stream);
 
+/* svdq_gemm_w4a4_lora_up with a caller workspace, for grids that leave the
+ * device mostly idle (the token rows one of several GPUs holds when a batch
+ * is split by rows).  Same operation and arguments as above (the Nunchaku
+ * engine caption (b) of the "svdq-int4-flux.1-dev" card), plus:
+ *   workspace (dev) workspace_bytes bytes, 16-byte aligned, owned by the
+ *             caller; its contents on entry do not matter; it must not be
+ *             used by another call that may run at the same time.
+ * svdq_gemm_workspace_size gives the bytes this call can use for the
+ * shape on the current device: 0 when the single-pass schedule runs
+ * anyway.  With a workspace of that size an INT4 grid whose tiles fill
+ * under half the workgroup slots (two per CU) and whose K loop has at
+ * least 16 stages of 128 k is cut along K: each part writes fp32 tile
+ * partials into the workspace, and a second kernel adds them in a fixed
+ * order and applies the up projection, the bias and the single rounding to
+ * bf16.  The result is deterministic, and within the same bounds as the
+ * single-pass schedule: its fp32 sums run in a different order.  A NULL
+ * or smaller workspace runs the single-pass schedule.  MXFP4 always runs
+ * the single-pass schedule. */
+SVDQ_API int svdq_gemm_workspace_size(int M, int N, int K, int precision, size_t* out_bytes);
+SVDQ_API int svdq_gemm_w4a4_lora_up_ws(const uint8_t* xq, const void* xs,
+                              const uint8_t* wq, const void* ws,
+                              const float* lora_act, const void* lora_up,
+                              const void* bias, void* y,
+                              int M, int N, int K, int rank, int precision,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* First layer of an MLP pair with its activation fused: the original
  * engine's model-specific paths include a fused GELU/MLP kernel (blog
  * "Nunchaku 4-bit inference in Diffusers", "Introducing Nunchaku Lite").

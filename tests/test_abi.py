@@ -185,6 +185,25 @@ def test_w4a16_calls_validate():
     assert p(FAKE, 100, 4, FAKE, FAKE) == bq.SVDQ_ERR_SHAPE
 
 
+def test_workspace_gemm_validates():
+    """svdq_gemm_w4a4_lora_up_ws applies the rules of svdq_gemm_w4a4_lora_up
+    and refuses a misaligned workspace; svdq_gemm_workspace_size checks its
+    shape and output pointer."""
+    L = bq.lib
+    g = L.svdq_gemm_w4a4_lora_up_ws
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 16, 16, 64, 16, 0, MIS, 1 << 20, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert g(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 16, 16, 64, 16, 0, FAKE, 1 << 20, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert g(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 16, 16, 64, 16, 0, FAKE, 1 << 20, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 16, 8, 64, 16, 0, FAKE, 1 << 20, None) == bq.SVDQ_ERR_SHAPE
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 16, 16, 96, 16, 0, None, 0, None) == bq.SVDQ_ERR_SHAPE
+    out = ctypes.c_size_t(7)
+    assert L.svdq_gemm_workspace_size(16, 16, 64, 0, None) == bq.SVDQ_ERR_INVALID_ARG
+    assert L.svdq_gemm_workspace_size(0, 16, 64, 0, ctypes.byref(out)) == bq.SVDQ_ERR_SHAPE
+    assert L.svdq_gemm_workspace_size(16, 16, 96, 0, ctypes.byref(out)) == bq.SVDQ_ERR_SHAPE
+    assert L.svdq_gemm_workspace_size(16, 16, 64, 2, ctypes.byref(out)) == bq.SVDQ_ERR_INVALID_ARG
+    assert out.value == 0
+
+
 @pytest.mark.skipif(_gpu_present(), reason="checks the no-device path")
 def test_no_device_gives_unsupported_device_not_a_crash():
     L = bq.lib
@@ -194,6 +213,10 @@ def test_no_device_gives_unsupported_device_not_a_crash():
     assert L.svdq_quantize_act_lora_down(FAKE, 16, 64, FAKE, FAKE, 16, 0, FAKE, FAKE, FAKE, None) == bq.SVDQ_ERR_UNSUPPORTED_DEVICE
     assert L.svdq_gemm_w4a4_lora_up(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 16, 16, 64, 16, 0, None) == bq.SVDQ_ERR_UNSUPPORTED_DEVICE
     assert L.svdq_debug_group_partials(FAKE, FAKE, 16, 16, 64, 0, 0, 1, 1, FAKE, None) == bq.SVDQ_ERR_UNSUPPORTED_DEVICE
+    assert L.svdq_gemm_w4a4_lora_up_ws(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 16, 16, 64, 16, 0, FAKE, 1 << 20,
+                                       None) == bq.SVDQ_ERR_UNSUPPORTED_DEVICE
+    out = ctypes.c_size_t(0)
+    assert L.svdq_gemm_workspace_size(576, 3072, 12288, 0, ctypes.byref(out)) == bq.SVDQ_ERR_UNSUPPORTED_DEVICE
     with pytest.raises(bq.SvdqError) as ei:
         bq.check(bq.SVDQ_ERR_UNSUPPORTED_DEVICE)
     assert ei.value.status == bq.SVDQ_ERR_UNSUPPORTED_DEVICE
