@@ -701,20 +701,26 @@ __device__ __forceinline__ void load_bias(float (&bv)[2][4][4], const uint16_t* 
 // already in LDS at upl.
 // PRE: the low-rank term and the bias are already in acc (lora_up_acc and
 // load_bias at the start of the tile).
-template <int EPI, bool UPL = false, bool PRE = false>
+template <int EPI, bool UPL = false, bool PRE = false, bool UPL_SYNC = false>
 __device__ __forceinline__ void epilogue_tile128(v16f (&acc)[2][2], const StageTile& stg,
                                                  const float* __restrict__ lact, const uint16_t* __restrict__ lup,
                                                  const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M,
                                                  int N, int rank, int n0, int m0, int wn, int wm, int l32, int h,
-                                                 int tid, const MlpOut& mo, const uint8_t* upl = nullptr) {
+                                                 int tid, const MlpOut& mo, const uint8_t* upl = nullptr,
+                                                 const uint8_t* upl_hi = nullptr, const uint8_t* upl_u = nullptr,
+                                                 const uint8_t* upl_b = nullptr) {
+  float bv[2][4][4];
   if constexpr (UPL) {
+    // lora_act rows 64-127 and the L2 rows may sit apart from rows 0-63
+    const uint8_t* const a_hi = upl_hi ? upl_hi : upl + 64 * 128;
+    const uint8_t* const u_rows = upl_u ? upl_u : upl + 16384;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       v4i ub[2], ua[2];
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
         const int r = wm * 64 + jt * 32 + l32;
-        const uint8_t* row = upl + r * 128;
+        const uint8_t* row = (wm ? a_hi : upl) + (jt * 32 + l32) * 128;
         const float4 f0 = *reinterpret_cast<const float4*>(row + (((4 * c + 2 * h) ^ swz8(r)) << 4));
         const float4 f1 = *reinterpret_cast<const float4*>(row + (((4 * c + 2 * h + 1) ^ swz8(r)) << 4));
         ub[jt] = m0 + r < M ? v4i{static_cast<int>(pack_bf16_rne(f0.x, f0.y)), static_cast<int>(pack_bf16_rne(f0.z, f0.w)),
@@ -724,7 +730,7 @@ __device__ __forceinline__ void epilogue_tile128(v16f (&acc)[2][2], const StageT
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
         const int r = wn * 64 + it * 32 + l32;
-        ua[it] = n0 + r < N ? *reinterpret_cast<const v4i*>(upl + 16384 + r * 64 + (((2 * c + h) ^ ((r >> 2) & 3)) << 4))
+        ua[it] = n0 + r < N ? *reinterpret_cast<const v4i*>(u_rows + r * 64 + (((2 * c + h) ^ ((r >> 2) & 3)) << 4))
                             : v4i{0, 0, 0, 0};
       }
 #pragma unroll
@@ -734,11 +740,27 @@ __device__ __forceinline__ void epilogue_tile128(v16f (&acc)[2][2], const StageT
           acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ua[it]),
                                                                 __builtin_bit_cast(v8bf, ub[jt]), acc[it][jt], 0, 0, 0);
     }
+    if constexpr (UPL_SYNC) {
+      // the bias of the tile's channels from LDS (bf16, channel n0 + i at
+      // byte 2 i; zeros without a bias), read before the barrier: the
+      // staging below overwrites LDS that other waves may still be reading
+#pragma unroll
+      for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int nl = wn * 64 + it * 32 + 8 * j + 4 * h;
+          const uint2 b2 = upl_b ? *reinterpret_cast<const uint2*>(upl_b + 2 * nl) : make_uint2(0u, 0u);
+          bv[it][j][0] = __uint_as_float(b2.x << 16);
+          bv[it][j][1] = __uint_as_float(b2.x & 0xFFFF0000u);
+          bv[it][j][2] = __uint_as_float(b2.y << 16);
+          bv[it][j][3] = __uint_as_float(b2.y & 0xFFFF0000u);
+        }
+      __syncthreads();
+    }
   }
   if constexpr (!PRE) lora_up_acc(acc, lact, lup, M, N, UPL ? 0 : rank, n0, m0, wn, wm, l32, h);
 
-  float bv[2][4][4];
-  load_bias(bv, PRE ? nullptr : bias, N, n0, wn, h);
+  if constexpr (!UPL_SYNC) load_bias(bv, PRE ? nullptr : bias, N, n0, wn, h);
 
   // Y = bf16(acc + bias), one rounding, into the staging tile [m][n]
 #pragma unroll
@@ -1080,7 +1102,7 @@ struct SplitOut {
   int per;
 };
 
-template <bool DEBUG, int EPI = 0, bool COARSE = false>
+template <bool DEBUG, int EPI = 0, bool COARSE = false, bool UPL = false>
 __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
     const uint8_t* __restrict__ xq, const uint16_t* __restrict__ xs,
     const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
@@ -1186,6 +1208,44 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
       wv[2 * i + 1] = op == 0 ? 0u : (e << 16);
     }
     s_words[st & 1][op][s_row] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+  };
+  // UPL (rank 32, plain epilogue): the tile's lora_act rows (128 x 32 fp32)
+  // and L2 rows (128 x 32 bf16) come straight into LDS while the K loop
+  // runs, in the layout of epilogue_tile128's UPL mode: lora_act rows 0-63
+  // into the W half and rows 64-127 into the X half of the ring slot that
+  // stage SL % 3 would use (no stage uses it after stage SL - 3), the L2
+  // rows into the tail of x_ring0 (past its code rows; only the epilogue's
+  // staging writes there).  Wave w moves lora_act rows 32 w .. +31 (four
+  // loads of 8 rows) and L2 rows 32 w .. +31 (two loads of 16 rows); rows
+  // past the matrix edge read zero; wave 0 adds one load of the bias.
+  // Six loads per wave (seven in wave 0), ordered by the kernel's own
+  // waits.
+  uint8_t* const upl_lo = wring(SL % kI4Slots);
+  uint8_t* const upl_hi = xring(SL % kI4Slots);
+  uint8_t* const upl_u = x_ring0 + kI4Op;
+  uint8_t* const upl_b = x_ring0 + kI4Op + 8192;
+  static_assert(kI4Op + 8192 + 1024 <= kI4Half, "L2 rows and bias fit in x_ring0 past its code rows");
+  auto upl_dma = [&]() __attribute__((always_inline)) {
+    if constexpr (UPL) {
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(lact + static_cast<size_t>(m0) * 32, static_cast<size_t>(M - m0) * 128);
+      const __amdgpu_buffer_rsrc_t ru = make_rsrc(lup + static_cast<size_t>(n0) * 32, static_cast<size_t>(N - n0) * 64);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int blk = 4 * wave + j, r = 8 * blk + (lane >> 3);
+        dma_b128(ra, lds_addr((blk < 8 ? upl_lo : upl_hi) + (blk & 7) * 1024), r * 128 + (((lane & 7) ^ swz8(r)) << 4), 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int blk = 2 * wave + j, r = 16 * blk + (lane >> 2);
+        dma_b128(ru, lds_addr(upl_u + blk * 1024), r * 64 + (((lane & 3) ^ ((r >> 2) & 3)) << 4), 0);
+      }
+      // wave 0 also moves the bias of channels n0 .. n0+511 (the tile uses
+      // the first 128; past N it reads zero) to the kilobyte after the L2 rows
+      if (wave == 0 && bias) {
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias + n0, static_cast<size_t>(N - n0) * 2);
+        dma_b128(rb, lds_addr(upl_b), 16 * lane, 0);
+      }
+    }
   };
 
   v16f acc[2][2];
@@ -1405,7 +1465,9 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   // for every load issued before them) does not also wait for stage 1;
   // then stage 0 complete and split.
   dma(0, Slot<0>{});
-  if constexpr (!DEBUG && EPI != kEpiPartial) {
+  if constexpr (UPL) {
+    if (SL == 1) upl_dma();
+  } else if constexpr (!DEBUG && EPI != kEpiPartial) {
     lora_up_acc(acc, lact, lup, M, N, rank, n0, m0, wn, wm, l32, h);
     float bv[2][4][4];
     load_bias(bv, bias, N, n0, wn, h);
@@ -1427,19 +1489,25 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
     constexpr int slot = decltype(slot_c)::value;
     constexpr int slot2 = (slot + 2) % kI4Slots;
     const bool ahead = st + 2 < SL;            // uniform
+    // UPL: the up-projection operands are issued with the second-to-last
+    // stage (six loads per wave behind stage st+1's, in the place of a
+    // stage st+2), so the waits below count them like a stage's loads
+    const bool up_now = UPL && st + 2 == SL;
     compute(slot, st & 1, 2 * (s_lo + st) + 1 >= G, 2 * st, [&]() __attribute__((always_inline)) {
       if (ahead) dma(st + 2, Slot<slot2>{});
+      if constexpr (UPL)
+        if (up_now) upl_dma();
       if constexpr (!DEBUG)
         if (st > 0) finish();
     });
     if (st + 1 < SL) {
-      if (ahead)
+      if (ahead || up_now)
         vm_wait<10>();
       else
         vm_wait<4>();
       split(st + 1);
     }
-    if (ahead)
+    if (ahead || up_now)
       lds_wait_barrier<6>();
     else
       lds_wait_barrier<0>();
@@ -1459,6 +1527,10 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
       const int r = 4 * (i & 3);
       dst[i * 256] = make_float4(a[r], a[r + 1], a[r + 2], a[r + 3]);
     }
+  } else if constexpr (UPL) {
+    epilogue_tile128<EPI, true, false, true>(acc, StageTile{reinterpret_cast<uint16_t*>(w_ring0), reinterpret_cast<uint16_t*>(x_ring0)},
+                                             lact, lup, bias, y, M, N, rank, n0, m0, wn, wm, l32, h, tid, mo, upl_lo,
+                                             upl_hi, upl_u, bias ? upl_b : nullptr);
   } else if constexpr (!DEBUG) {
     epilogue_tile128<EPI, false, true>(acc, StageTile{reinterpret_cast<uint16_t*>(w_ring0), reinterpret_cast<uint16_t*>(x_ring0)}, lact,
                           lup, bias, y, M, N, rank, n0, m0, wn, wm, l32, h, tid, mo);
@@ -1847,9 +1919,18 @@ extern "C" int svdq_launch_gemm_w4a4_lora_up(const uint8_t* xq, const void* xs, 
                        static_cast<uint16_t*>(y), M, N, K, rank);
     return static_cast<int>(hipGetLastError());
   }
-  // long K loops take the coarse MFMA/VALU phases (see k2_gemm_int4)
+  // long K loops take the coarse MFMA/VALU phases (see k2_gemm_int4); on
+  // the fine schedule rank 32 brings its up-projection operands and the
+  // bias into LDS during the K loop (on the coarse one that measured ~1 %
+  // slower, on the fine one ~4 % faster, FLUX fc2 / fc1)
   if (K >= kI4CoarseMinK)
     hipLaunchKernelGGL((k2_gemm_int4<false, 0, true>), dim3(tiles), dim3(kMxThreads), 0,
+                       static_cast<hipStream_t>(stream), xq, static_cast<const uint16_t*>(xs), wq,
+                       static_cast<const uint16_t*>(ws), lora_act, static_cast<const uint16_t*>(lora_up),
+                       static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), M, N, K, rank, 0, 0, 0, 0,
+                       nullptr, MlpOut{}, SplitOut{});
+  else if (rank == 32)
+    hipLaunchKernelGGL((k2_gemm_int4<false, 0, false, true>), dim3(tiles), dim3(kMxThreads), 0,
                        static_cast<hipStream_t>(stream), xq, static_cast<const uint16_t*>(xs), wq,
                        static_cast<const uint16_t*>(ws), lora_act, static_cast<const uint16_t*>(lora_up),
                        static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), M, N, K, rank, 0, 0, 0, 0,
