@@ -401,9 +401,11 @@ __global__ __launch_bounds__(256) void k1_quant_down_int4(
   }
 }
 
+// lora_act cleared before kernel 1's atomic slice sums: 16 bytes per thread
+// (n is a multiple of 16 floats: the rank is)
 __global__ void fill_zero_f32(float* __restrict__ p, size_t n) {
   const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0.f;
+  if (4 * i < n) reinterpret_cast<float4*>(p)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 // ---------------------------------------------------------------------------
@@ -742,19 +744,24 @@ __device__ __forceinline__ void epilogue_tile128(v16f (&acc)[2][2], const StageT
     }
     if constexpr (UPL_SYNC) {
       // the bias of the tile's channels from LDS (bf16, channel n0 + i at
-      // byte 2 i; zeros without a bias), read before the barrier: the
-      // staging below overwrites LDS that other waves may still be reading
+      // byte 2 i) or, without upl_b, from memory (zeros without a bias),
+      // read before the barrier: the staging below overwrites LDS that
+      // other waves may still be reading
+      if (upl_b) {
 #pragma unroll
-      for (int it = 0; it < 2; ++it)
+        for (int it = 0; it < 2; ++it)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int nl = wn * 64 + it * 32 + 8 * j + 4 * h;
-          const uint2 b2 = upl_b ? *reinterpret_cast<const uint2*>(upl_b + 2 * nl) : make_uint2(0u, 0u);
-          bv[it][j][0] = __uint_as_float(b2.x << 16);
-          bv[it][j][1] = __uint_as_float(b2.x & 0xFFFF0000u);
-          bv[it][j][2] = __uint_as_float(b2.y << 16);
-          bv[it][j][3] = __uint_as_float(b2.y & 0xFFFF0000u);
-        }
+          for (int j = 0; j < 4; ++j) {
+            const int nl = wn * 64 + it * 32 + 8 * j + 4 * h;
+            const uint2 b2 = *reinterpret_cast<const uint2*>(upl_b + 2 * nl);
+            bv[it][j][0] = __uint_as_float(b2.x << 16);
+            bv[it][j][1] = __uint_as_float(b2.x & 0xFFFF0000u);
+            bv[it][j][2] = __uint_as_float(b2.y << 16);
+            bv[it][j][3] = __uint_as_float(b2.y & 0xFFFF0000u);
+          }
+      } else {
+        load_bias(bv, bias, N, n0, wn, h);
+      }
       __syncthreads();
     }
   }
@@ -1240,8 +1247,11 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
         dma_b128(ru, lds_addr(upl_u + blk * 1024), r * 64 + (((lane & 3) ^ ((r >> 2) & 3)) << 4), 0);
       }
       // wave 0 also moves the bias of channels n0 .. n0+511 (the tile uses
-      // the first 128; past N it reads zero) to the kilobyte after the L2 rows
-      if (wave == 0 && bias) {
+      // the first 128; past N it reads zero) to the kilobyte after the L2
+      // rows.  Even N only: the buffer bounds a load dword by dword, so with
+      // odd N the last channel's dword would read zero; odd N takes the
+      // bias from memory in the epilogue.
+      if (wave == 0 && bias && (N & 1) == 0) {
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias + n0, static_cast<size_t>(N - n0) * 2);
         dma_b128(rb, lds_addr(upl_b), 16 * lane, 0);
       }
@@ -1530,7 +1540,7 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_int4(
   } else if constexpr (UPL) {
     epilogue_tile128<EPI, true, false, true>(acc, StageTile{reinterpret_cast<uint16_t*>(w_ring0), reinterpret_cast<uint16_t*>(x_ring0)},
                                              lact, lup, bias, y, M, N, rank, n0, m0, wn, wm, l32, h, tid, mo, upl_lo,
-                                             upl_hi, upl_u, bias ? upl_b : nullptr);
+                                             upl_hi, upl_u, bias && (N & 1) == 0 ? upl_b : nullptr);
   } else if constexpr (!DEBUG) {
     epilogue_tile128<EPI, false, true>(acc, StageTile{reinterpret_cast<uint16_t*>(w_ring0), reinterpret_cast<uint16_t*>(x_ring0)}, lact,
                           lup, bias, y, M, N, rank, n0, m0, wn, wm, l32, h, tid, mo);
@@ -1739,7 +1749,7 @@ hipError_t launch_k1(const void* x, int M, int K, const float* sinv, const void*
   const bool atomic = RT > 0 && slices > 1;
   if (atomic) {
     const size_t n = static_cast<size_t>(M) * RT * 16;
-    hipLaunchKernelGGL(fill_zero_f32, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, lact, n);
+    hipLaunchKernelGGL(fill_zero_f32, dim3(static_cast<unsigned>((n / 4 + 255) / 256)), dim3(256), 0, st, lact, n);
     hipLaunchKernelGGL((k1_quant_down_int4<RT, true, QMODE>), grid, block, lds, st, static_cast<const uint16_t*>(x), M, K,
                        sinv, static_cast<const uint16_t*>(ldown), xq, xs, lact, ks);
   } else {
@@ -2024,7 +2034,7 @@ extern "C" int svdq_launch_mlp_gemm_gelu_quant(const uint8_t* xq, const void* xs
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (rank2 > 0) {
     const size_t n = static_cast<size_t>(M) * rank2;
-    hipLaunchKernelGGL(fill_zero_f32, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, lora_act2, n);
+    hipLaunchKernelGGL(fill_zero_f32, dim3(static_cast<unsigned>((n / 4 + 255) / 256)), dim3(256), 0, st, lora_act2, n);
   }
   const int tiles = ((N + kTile - 1) / kTile) * ((M + kTile - 1) / kTile);
   const MlpOut mo{smooth_inv2, static_cast<const uint16_t*>(lora_down2), rank2, xq2, static_cast<uint16_t*>(xs2),

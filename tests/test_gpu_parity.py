@@ -85,6 +85,10 @@ SMALL = [
     (130, 64, 150, 16, 9, True),      # one group (one half stage) with the low-rank branch
     (257, 128, 129, 32, 10, False),   # one stage, ragged M and N
     (33, 8192, 131, 16, 11, True),    # coarse schedule with odd N (element stores)
+    (70, 320, 131, 32, 12, True),     # rank 32 (up projection and bias via LDS), odd N, odd group count
+    (65, 256, 34, 32, 13, True),      # rank 32, two stages, ragged even N (bias via LDS)
+    (40, 128, 45, 32, 14, True),      # rank 32, one stage (operands issued with stage 0), odd N
+    (130, 128, 160, 32, 15, False),   # rank 32, one stage, no bias
 ]
 
 
