@@ -804,7 +804,10 @@ __device__ __forceinline__ void epilogue_tile128(v16f (&acc)[2][2], const StageT
       const uint4 v = *reinterpret_cast<const uint4*>(stg.row(r) + c8);
       uint16_t* dst = y + static_cast<size_t>(m) * N + n;
       if ((N % 8) == 0) {
-        *reinterpret_cast<uint4*>(dst) = v;
+        // non-temporal: Y is not read again here, and streaming it past the
+        // caches keeps the operand panels resident (measured: INT4 fc1 -3 %,
+        // MXFP4 fc1 -7 %, bit-identical output)
+        __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(dst));
       } else {
         const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
