@@ -151,8 +151,13 @@ __device__ __forceinline__ uint4 pack_codes_fp6(const float (&x)[4][8], float in
   return make_uint4(d[0] | (d[2] & kZ0), d[1] | (d[2] & kZ1), d[3] | (d[5] & kZ0), d[4] | (d[5] & kZ1));
 }
 
+// Ranks up to 48 are held to four workgroups per CU (at most 128 VGPRs,
+// four waves per SIMD): unbounded, the compiler took 136 VGPRs at rank 32,
+// three waves per SIMD, and the launch slots fell under the ~1024-workgroup
+// grid (bounded: FLUX fc1 17.3 -> 15.9 us, fc2 45 -> 43 us, no spill).
+// Larger ranks would spill under that bound and keep the compiler's choice.
 template <int RT, bool ATOMIC, int QMODE = kQuantInt4>
-__global__ __launch_bounds__(256) void k1_quant_down_int4(
+__global__ __launch_bounds__(256, (RT <= 3 ? 4 : 1)) void k1_quant_down_int4(
     const uint16_t* __restrict__ x, int M, int K, const float* __restrict__ sinv,
     const uint16_t* __restrict__ ldown, uint8_t* __restrict__ xq, void* __restrict__ xs_,
     float* __restrict__ lact, int ks) {
