@@ -747,32 +747,32 @@ __device__ __forceinline__ void epilogue_tile128(v16f (&acc)[2][2], const StageT
           acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ua[it]),
                                                                 __builtin_bit_cast(v8bf, ub[jt]), acc[it][jt], 0, 0, 0);
     }
+    // the bias of the tile's channels from LDS (bf16, channel n0 + i at
+    // byte 2 i) or, without upl_b, from memory (zeros without a bias);
+    // with UPL_SYNC read before the barrier: the staging below overwrites
+    // LDS that other waves may still be reading
+    if (upl_b) {
+#pragma unroll
+      for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int nl = wn * 64 + it * 32 + 8 * j + 4 * h;
+          const uint2 b2 = *reinterpret_cast<const uint2*>(upl_b + 2 * nl);
+          bv[it][j][0] = __uint_as_float(b2.x << 16);
+          bv[it][j][1] = __uint_as_float(b2.x & 0xFFFF0000u);
+          bv[it][j][2] = __uint_as_float(b2.y << 16);
+          bv[it][j][3] = __uint_as_float(b2.y & 0xFFFF0000u);
+        }
+    } else {
+      load_bias(bv, bias, N, n0, wn, h);
+    }
     if constexpr (UPL_SYNC) {
-      // the bias of the tile's channels from LDS (bf16, channel n0 + i at
-      // byte 2 i) or, without upl_b, from memory (zeros without a bias),
-      // read before the barrier: the staging below overwrites LDS that
-      // other waves may still be reading
-      if (upl_b) {
-#pragma unroll
-        for (int it = 0; it < 2; ++it)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int nl = wn * 64 + it * 32 + 8 * j + 4 * h;
-            const uint2 b2 = *reinterpret_cast<const uint2*>(upl_b + 2 * nl);
-            bv[it][j][0] = __uint_as_float(b2.x << 16);
-            bv[it][j][1] = __uint_as_float(b2.x & 0xFFFF0000u);
-            bv[it][j][2] = __uint_as_float(b2.y << 16);
-            bv[it][j][3] = __uint_as_float(b2.y & 0xFFFF0000u);
-          }
-      } else {
-        load_bias(bv, bias, N, n0, wn, h);
-      }
       __syncthreads();
     }
   }
   if constexpr (!PRE) lora_up_acc(acc, lact, lup, M, N, UPL ? 0 : rank, n0, m0, wn, wm, l32, h);
 
-  if constexpr (!UPL_SYNC) load_bias(bv, PRE ? nullptr : bias, N, n0, wn, h);
+  if constexpr (!UPL) load_bias(bv, PRE ? nullptr : bias, N, n0, wn, h);
 
   // Y = bf16(acc + bias), one rounding, into the staging tile [m][n]
 #pragma unroll
@@ -835,7 +835,7 @@ constexpr int kMxdRowB = 128;                      // LDS bytes per row and stag
 constexpr int kMxdOp = kTile * kMxdRowB;           // one operand's rows
 constexpr int kMxdSlot = 2 * kMxdOp + 2 * 8 * kTile;   // W rows, X rows, then scales [W|X][block][row]
 static_assert(kMxdSlot >= kTile * kMxYRow * 2, "output staging fits in one slot of the ring");
-static_assert(kMxdSlot >= 16384 + 8192, "rank-32 up-projection operands fit in one slot");
+static_assert(kMxdSlot >= 16384 + 8192 + 1024, "rank-32 up-projection operands and the bias fit in one slot");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -846,8 +846,8 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // rows) and L2 rows 32 w .. +31 (two loads of 16 rows); the caller waits
 // (vmcnt) and synchronises before the epilogue reads them.
 __device__ __forceinline__ void upl_issue(uint8_t* dst, const float* __restrict__ lact,
-                                          const uint16_t* __restrict__ lup, int M, int N, int m0, int n0, int wave,
-                                          int lane) {
+                                          const uint16_t* __restrict__ lup, const uint16_t* __restrict__ bias,
+                                          int M, int N, int m0, int n0, int wave, int lane) {
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(lact + static_cast<size_t>(m0) * 32, static_cast<size_t>(M - m0) * 128);
   const __amdgpu_buffer_rsrc_t ru = make_rsrc(lup + static_cast<size_t>(n0) * 32, static_cast<size_t>(N - n0) * 64);
 #pragma unroll
@@ -861,6 +861,13 @@ __device__ __forceinline__ void upl_issue(uint8_t* dst, const float* __restrict_
     const int blk = 2 * wave + j, r = 16 * blk + (lane >> 2);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (lds_ptr_t)(dst + 16384 + blk * 1024), 16,
                                              r * 64 + (((lane & 3) ^ ((r >> 2) & 3)) << 4), 0, 0, 0);
+  }
+  // wave 0: the bias of channels n0 .. n0+511 (the tile uses the first 128)
+  // into the kilobyte after the L2 rows; even N only (a buffer load bounds
+  // each dword, so with odd N the last channel's dword would read zero)
+  if (wave == 0 && bias && (N & 1) == 0) {
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias + n0, static_cast<size_t>(N - n0) * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(dst + 16384 + 8192), 16, 16 * lane, 0, 0, 0);
   }
 }
 
@@ -988,7 +995,7 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_mxfp4(
   // output is staged in the other slot.
   const bool upl = rank == 32;
   auto issue_up = [&](auto buf_c) {
-    upl_issue(&lds_c[decltype(buf_c)::value][0], lact, lup, M, N, m0, n0, wave, lane);
+    upl_issue(&lds_c[decltype(buf_c)::value][0], lact, lup, bias, M, N, m0, n0, wave, lane);
   };
   issue(0, Slot<0>{});
   __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this wave's stage-0 data is in LDS
@@ -1009,7 +1016,8 @@ __global__ __launch_bounds__(kMxThreads, 2) void k2_gemm_mxfp4(
   const int last = (S - 1) & 1;
   if (upl)
     epilogue_tile128<0, true>(acc, stage_tile(reinterpret_cast<uint16_t*>(&lds_c[last][0])), lact, lup, bias, y, M, N, rank, n0,
-                              m0, wn, wm, l32, h, tid, MlpOut{}, &lds_c[1 - last][0]);
+                              m0, wn, wm, l32, h, tid, MlpOut{}, &lds_c[1 - last][0], nullptr, nullptr,
+                              bias && (N & 1) == 0 ? &lds_c[1 - last][16384 + 8192] : nullptr);
   else
     epilogue_tile128<0>(acc, stage_tile(reinterpret_cast<uint16_t*>(&lds_c[0][0])), lact, lup, bias, y, M, N, rank, n0,
                         m0, wn, wm, l32, h, tid, MlpOut{});

@@ -26,6 +26,8 @@ SMALL_MX = [
     (64, 384, 64, 64, 14, False),     # exactly the ring's 3 stages
     (520, 1024, 264, 16, 15, True),
     (40, 4096, 272, 256, 16, True),   # largest rank
+    (70, 384, 131, 32, 17, True),     # rank 32 (up projection via LDS), odd N: bias from memory
+    (65, 256, 34, 32, 18, True),      # rank 32, ragged even N: bias via LDS
 ]
 
 
